@@ -1,0 +1,269 @@
+"""CPU oracle for the ParallelKittens one-GPU hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package.  The product library (``gemm_tile_granular_bf16_amd``) never imports, links
+or calls it, and the two share no code: the oracle is plain C (``pk_oracle.c``) evaluated in
+IEEE binary64, loaded here through ctypes.
+
+What each function computes, and the passage it follows:
+
+* ``gemm`` -- the AG+GEMM local share: a plain product of the gathered row-chunks of A with the
+  local column shard of B ("Loads and Loads of Fluffy Kittens" summary, Results: AG+GEMM with
+  local shape N x N/8 x N).  Pinned by closed forms, integer exactness, brute force and an
+  independent library product (tests/test_oracle_gemm.py).
+* ``reduce`` -- the receiving side of GEMM+RS / GEMM+AR: each output tile "is sent and atomically
+  added at the destination" (same page, Method), i.e. D0 + sum_p A_p B_p.  Pinned by integer
+  exactness, the K-concatenation identity and closed forms (tests/test_oracle_reduce.py).
+* ``round_bf16`` / ``cast_f32_bf16`` -- round to nearest bf16, ties to even; the bf16 cast after
+  the all-reduce.  Pinned exhaustively against hand-derived cases and an independent library
+  conversion (tests/test_oracle_bf16.py, tests/golden/bf16_rne.txt).
+* ``dispatch`` -- token dispatch for expert parallelism (same page, Key claims and Results:
+  token-dispatch + GEMM, top_k=8, 256 experts): a stable counting sort of routing slots by local
+  expert.  Pinned against a library stable sort, invariants and special cases, and a hand-worked
+  example (tests/test_oracle_dispatch.py, tests/golden/dispatch_small.txt).
+* ``grouped_gemm`` -- the per-expert product over dispatched rows.  Pinned by the
+  selection-weight identity, the one-expert reduction to ``gemm`` and brute force
+  (tests/test_oracle_grouped.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Iterable, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "pk_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_pk_oracle.so")
+
+
+def compile_library(src: str, out: str) -> str:
+    """Compile C oracle source ``src`` into shared library ``out`` with the host C compiler."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-pthread",
+           "-shared", "-fPIC", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle into ``oracle/_pk_oracle.so``."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    return compile_library(SOURCE, _LIB_PATH)
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses by default: the CPUs this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _bf16(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 operands are passed as uint16 bit patterns, got %s" % a.dtype)
+    return np.ascontiguousarray(a)
+
+
+class Oracle:
+    """The oracle's entry points bound to one compiled copy of ``pk_oracle.c``."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.pk_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.pk_oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.pk_oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.pk_oracle_f64_to_bf16.restype = ctypes.c_uint16
+        lib.pk_oracle_round_bf16.argtypes = [p, i64, p]
+        lib.pk_oracle_round_bf16.restype = None
+        lib.pk_oracle_cast_f32_bf16.argtypes = [p, i64, p]
+        lib.pk_oracle_cast_f32_bf16.restype = None
+        lib.pk_oracle_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i32]
+        lib.pk_oracle_gemm.restype = i32
+        lib.pk_oracle_reduce.argtypes = [i64, i64, i32, p, p, p, p, p, p, i64, p, i64, i32]
+        lib.pk_oracle_reduce.restype = i32
+        lib.pk_oracle_dispatch.argtypes = [i64, i32, p, i32, i32, i32, p, p, p]
+        lib.pk_oracle_dispatch.restype = i64
+        lib.pk_oracle_grouped_gemm.argtypes = [i32, p, p, i32, p, i64, i64, p, i64, p, i64, i32]
+        lib.pk_oracle_grouped_gemm.restype = i32
+        self.lib = lib
+        self.path = path
+
+    # -- bf16 encode / decode ------------------------------------------------------------- #
+
+    def bf16_to_f64(self, bits) -> np.ndarray:
+        """Exact value of each bf16 bit pattern, as binary64."""
+        b = _bf16(bits)
+        flat = b.reshape(-1).tolist()
+        out = np.array([self.lib.pk_oracle_bf16_to_f64(h) for h in flat], dtype=np.float64)
+        return out.reshape(b.shape)
+
+    def round_bf16(self, x) -> np.ndarray:
+        """Round binary64 values to the nearest bf16 (ties to even); uint16 bit patterns."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.pk_oracle_round_bf16(_ptr(x), x.size, _ptr(out))
+        return out
+
+    def cast_f32_bf16(self, x) -> np.ndarray:
+        """The all-reduce output cast: binary32 -> bf16, round to nearest even (uint16 bits)."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.pk_oracle_cast_f32_bf16(_ptr(x), x.size, _ptr(out))
+        return out
+
+    # -- products ------------------------------------------------------------------------- #
+
+    def gemm(self, A, B, nthreads: int = 0) -> np.ndarray:
+        """R = A B in binary64 (A: M x K bf16 bits, B: K x N bf16 bits)."""
+        A, B = _bf16(A), _bf16(B)
+        if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
+            raise ValueError("gemm shapes %s x %s" % (A.shape, B.shape))
+        M, K = A.shape
+        N = B.shape[1]
+        R = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.pk_oracle_gemm(M, N, K, _ptr(A), K, _ptr(B), N, _ptr(R), N,
+                                     nthreads or default_threads())
+        if rc:
+            raise RuntimeError("pk_oracle_gemm failed (%d)" % rc)
+        return R
+
+    def gemm_rows(self, A, B, rows: Iterable[int], nthreads: int = 0) -> np.ndarray:
+        """The product restricted to the listed output rows (sampled checks at full size)."""
+        A = _bf16(A)
+        idx = np.asarray(list(rows), dtype=np.int64)
+        return self.gemm(np.ascontiguousarray(A[idx]), B, nthreads)
+
+    def reduce(self, D0, producers: Sequence, nthreads: int = 0) -> np.ndarray:
+        """R = D0 + sum_p A_p B_p in binary64.
+
+        ``D0`` is the binary32 destination as it stood before the producers (M x N) or None for
+        zero; ``producers`` is a sequence of (A_p, B_p) bf16 bit-pattern pairs.
+        """
+        prods = [(_bf16(a), _bf16(b)) for a, b in producers]
+        if not prods and D0 is None:
+            raise ValueError("reduce needs D0 or at least one producer")
+        if prods:
+            M, N = prods[0][0].shape[0], prods[0][1].shape[1]
+        else:
+            M, N = np.asarray(D0).shape
+        for a, b in prods:
+            if a.shape[0] != M or b.shape[1] != N or a.shape[1] != b.shape[0]:
+                raise ValueError("producer shapes differ: %s x %s" % (a.shape, b.shape))
+        n = len(prods)
+        K = (ctypes.c_int64 * max(n, 1))(*[a.shape[1] for a, _ in prods])
+        Ap = (ctypes.c_void_p * max(n, 1))(*[_ptr(a) for a, _ in prods])
+        lda = (ctypes.c_int64 * max(n, 1))(*[a.shape[1] for a, _ in prods])
+        Bp = (ctypes.c_void_p * max(n, 1))(*[_ptr(b) for _, b in prods])
+        ldb = (ctypes.c_int64 * max(n, 1))(*[b.shape[1] for _, b in prods])
+        if D0 is not None:
+            D0 = np.ascontiguousarray(np.asarray(D0, dtype=np.float32))
+            if D0.shape != (M, N):
+                raise ValueError("D0 shape %s, expected %s" % (D0.shape, (M, N)))
+        R = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.pk_oracle_reduce(M, N, n, K, Ap, lda, Bp, ldb,
+                                       _ptr(D0) if D0 is not None else None, N, _ptr(R), N,
+                                       nthreads or default_threads())
+        if rc:
+            raise RuntimeError("pk_oracle_reduce failed (%d)" % rc)
+        return R
+
+    # -- expert parallelism --------------------------------------------------------------- #
+
+    def dispatch(self, topk_ids, num_experts: int, expert_begin: int, num_local: int):
+        """Stable counting sort of routing slots by local expert.
+
+        Returns (counts[num_local], offsets[num_local+1], perm[rows]) as int32 arrays; perm
+        holds flat slot indices t*top_k + k in expert-major, ascending-slot order.
+        """
+        ids = np.ascontiguousarray(np.asarray(topk_ids, dtype=np.int32))
+        if ids.ndim != 2:
+            raise ValueError("topk_ids must be T x top_k")
+        T, top_k = ids.shape
+        counts = np.zeros(max(num_local, 1), dtype=np.int32)
+        offsets = np.zeros(num_local + 1, dtype=np.int32)
+        perm = np.zeros(max(T * top_k, 1), dtype=np.int32)
+        rows = self.lib.pk_oracle_dispatch(T, top_k, _ptr(ids), num_experts, expert_begin,
+                                           num_local, _ptr(counts), _ptr(offsets), _ptr(perm))
+        if rows < 0:
+            raise RuntimeError("pk_oracle_dispatch: bad arguments")
+        return counts[:num_local].copy(), offsets, perm[:rows].copy()
+
+    def grouped_gemm(self, offsets, perm, top_k: int, X, W, nthreads: int = 0) -> np.ndarray:
+        """Y[j] = X[perm[j] // top_k] . W[e] for rows j of expert e (binary64, rows x N)."""
+        X, W = _bf16(X), _bf16(W)
+        offsets = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
+        perm = np.ascontiguousarray(np.asarray(perm, dtype=np.int32))
+        num_local = offsets.shape[0] - 1
+        if W.ndim != 3 or W.shape[0] != num_local or X.shape[1] != W.shape[1]:
+            raise ValueError("grouped shapes X %s W %s num_local %d" % (X.shape, W.shape,
+                                                                     num_local))
+        K, N = W.shape[1], W.shape[2]
+        rows = int(offsets[-1]) if num_local > 0 else 0
+        Y = np.empty((rows, N), dtype=np.float64)
+        rc = self.lib.pk_oracle_grouped_gemm(num_local, _ptr(offsets), _ptr(perm), top_k,
+                                             _ptr(X), X.shape[1], K, _ptr(W), N, _ptr(Y), N,
+                                             nthreads or default_threads())
+        if rc:
+            raise RuntimeError("pk_oracle_grouped_gemm failed (%d)" % rc)
+        return Y
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``pk_oracle.c`` (compiled on first use if missing)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _default = Oracle(_LIB_PATH)
+    return _default
+
+
+def bf16_to_f64(bits):
+    return default().bf16_to_f64(bits)
+
+
+def round_bf16(x):
+    return default().round_bf16(x)
+
+
+def cast_f32_bf16(x):
+    return default().cast_f32_bf16(x)
+
+
+def gemm(A, B, nthreads: int = 0):
+    return default().gemm(A, B, nthreads)
+
+
+def gemm_rows(A, B, rows, nthreads: int = 0):
+    return default().gemm_rows(A, B, rows, nthreads)
+
+
+def reduce(D0, producers, nthreads: int = 0):
+    return default().reduce(D0, producers, nthreads)
+
+
+def dispatch(topk_ids, num_experts: int, expert_begin: int, num_local: int):
+    return default().dispatch(topk_ids, num_experts, expert_begin, num_local)
+
+
+def grouped_gemm(offsets, perm, top_k: int, X, W, nthreads: int = 0):
+    return default().grouped_gemm(offsets, perm, top_k, X, W, nthreads)
+
+
+def _load():
+    return default().lib

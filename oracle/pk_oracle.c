@@ -1,0 +1,255 @@
+/*
+ * pk_oracle.c -- plain, slow, obviously-correct CPU reference for the one-GPU share of the
+ * ParallelKittens compute-communication kernels.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this file:
+ * only the test-suite, the smoke check and the CPU-baseline leg of the benchmark do.  It shares
+ * no code, header, table or helper with the HIP library.
+ *
+ * What is computed (pages: "Loads and Loads of Fluffy Kittens" summary, sections "Method" and
+ * "Results"; ParallelKittens arXiv abstract):
+ *   - AG+GEMM local share: a plain matrix product of the gathered row-chunks of A with the local
+ *     column shard of B (local shape N x N/8 x N);
+ *   - GEMM+RS / GEMM+AR receiving side: each output tile of the local product "is sent and
+ *     atomically added at the destination", i.e. D_final = D_initial + sum over producers of A_p B_p
+ *     (a sum; no order is specified);
+ *   - token dispatch + expert GEMM: routed tokens are grouped per expert and multiplied by that
+ *     expert's weight matrix.
+ *
+ * Arithmetic: every product and sum is taken in IEEE binary64 over the bf16 inputs decoded
+ * exactly; sums run in ascending index order.  bf16 outputs are the binary64 result rounded once,
+ * to nearest with ties to even (IEEE 754 roundTiesToEven applied to the bf16 format: 8 exponent
+ * bits, 8 significant bits).  The host must run in the default rounding mode.
+ *
+ * Parallelism: output rows are split over POSIX threads; each output element is still computed
+ * by one thread in ascending k, so the result does not depend on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------------------------------ */
+/* bf16 <-> binary64                                                                           */
+/* ------------------------------------------------------------------------------------------ */
+
+/* bf16 is the upper half of an IEEE binary32 word: sign(1) exponent(8) fraction(7). */
+double pk_oracle_bf16_to_f64(uint16_t h) {
+    uint32_t w = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f; /* exact: binary32 -> binary64 */
+}
+
+/* Encode an exactly representable, positive, finite bf16 magnitude. */
+static uint16_t encode_bf16_magnitude(double r) {
+    if (r < 0x1p-126) {
+        /* subnormal: value = fraction * 2^-133, fraction < 128 */
+        return (uint16_t)(r / 0x1p-133);
+    }
+    int e;
+    double f = frexp(r, &e); /* r = f * 2^e, 0.5 <= f < 1 */
+    int biased = (e - 1) + 127;
+    if (biased >= 255) return 0x7f80;
+    int frac = (int)(f * 256.0) - 128; /* 8 significant bits: f*256 is an integer in [128,256) */
+    return (uint16_t)((biased << 7) | frac);
+}
+
+/* Round a binary64 value to the nearest bf16, ties to even.  NaN -> quiet NaN, overflow -> inf. */
+uint16_t pk_oracle_f64_to_bf16(double x) {
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x)) return (uint16_t)(sign | 0x7fc0);
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint16_t)(sign | 0x7f80);
+    int e;
+    frexp(a, &e);
+    int lead = e - 1;               /* a lies in [2^lead, 2^(lead+1)) */
+    if (lead < -126) lead = -126;   /* below the normal range the spacing stays 2^-133 */
+    double quantum = ldexp(1.0, lead - 7); /* spacing of bf16 values around a */
+    double n = nearbyint(a / quantum);     /* a/quantum is exact; ties go to the even integer */
+    double r = n * quantum;                /* exact */
+    if (r >= 0x1p128) return (uint16_t)(sign | 0x7f80);
+    return (uint16_t)(sign | encode_bf16_magnitude(r));
+}
+
+void pk_oracle_round_bf16(const double* x, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = pk_oracle_f64_to_bf16(x[i]);
+}
+
+/* The cast pass of GEMM+AR: binary32 destination -> bf16, round to nearest even. */
+void pk_oracle_cast_f32_bf16(const float* x, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = pk_oracle_f64_to_bf16((double)x[i]);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Dense product over threads                                                                  */
+/* ------------------------------------------------------------------------------------------ */
+
+typedef struct {
+    int64_t row_begin, row_end, N, K;
+    const uint16_t* A; int64_t lda;
+    const double* Bd; /* B decoded to binary64, K x N, dense */
+    double* R; int64_t ldr;
+    int accumulate; /* 0: R = A B ; 1: R += A B */
+} gemm_job;
+
+/* R[i][j] (+)= sum_{k ascending} A[i][k] * B[k][j].  The i-k-j loop keeps, for each fixed (i,j),
+   the additions in ascending k, one binary64 rounding per addition. */
+static void* gemm_rows(void* arg) {
+    gemm_job* g = (gemm_job*)arg;
+    for (int64_t i = g->row_begin; i < g->row_end; ++i) {
+        double* r = g->R + i * g->ldr;
+        if (!g->accumulate)
+            for (int64_t j = 0; j < g->N; ++j) r[j] = 0.0;
+        for (int64_t k = 0; k < g->K; ++k) {
+            double a = pk_oracle_bf16_to_f64(g->A[i * g->lda + k]);
+            const double* b = g->Bd + k * g->N;
+            for (int64_t j = 0; j < g->N; ++j) r[j] += a * b[j];
+        }
+    }
+    return NULL;
+}
+
+static int resolve_threads(int nthreads, int64_t rows) {
+    if (nthreads <= 0) {
+        long n = sysconf(_SC_NPROCESSORS_ONLN);
+        nthreads = n > 0 ? (int)n : 1;
+    }
+    if (nthreads > 256) nthreads = 256;
+    if (rows < nthreads) nthreads = rows > 0 ? (int)rows : 1;
+    return nthreads;
+}
+
+static double* decode_matrix(int64_t rows, int64_t cols, const uint16_t* X, int64_t ldx) {
+    double* d = (double*)malloc(sizeof(double) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+    if (!d) return NULL;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j) d[i * cols + j] = pk_oracle_bf16_to_f64(X[i * ldx + j]);
+    return d;
+}
+
+/* Rows of R split over threads; B given already decoded. */
+static void run_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                     const double* Bd, double* R, int64_t ldr, int accumulate, int nthreads) {
+    nthreads = resolve_threads(nthreads, M);
+    gemm_job jobs[256];
+    pthread_t tid[256];
+    int started[256];
+    int64_t per = (M + nthreads - 1) / nthreads;
+    int used = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        int64_t b = t * per, e = b + per < M ? b + per : M;
+        if (b >= e) break;
+        jobs[t] = (gemm_job){b, e, N, K, A, lda, Bd, R, ldr, accumulate};
+        started[t] = pthread_create(&tid[t], NULL, gemm_rows, &jobs[t]) == 0;
+        if (!started[t]) gemm_rows(&jobs[t]);
+        ++used;
+    }
+    for (int t = 0; t < used; ++t)
+        if (started[t]) pthread_join(tid[t], NULL);
+}
+
+static int run_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                    const uint16_t* B, int64_t ldb, double* R, int64_t ldr, int accumulate,
+                    int nthreads) {
+    if (M < 0 || N < 0 || K < 0) return 1;
+    if (M == 0 || N == 0) return 0;
+    double* Bd = decode_matrix(K, N, B, ldb);
+    if (!Bd) return 2;
+    run_rows(M, N, K, A, lda, Bd, R, ldr, accumulate, nthreads);
+    free(Bd);
+    return 0;
+}
+
+/* GEMM (AG+GEMM local share, and the expert product): R = A B, A MxK bf16, B KxN bf16, both
+   row-major with leading dimensions in elements; R MxN binary64 with leading dimension ldr. */
+int pk_oracle_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                   const uint16_t* B, int64_t ldb, double* R, int64_t ldr, int nthreads) {
+    return run_gemm(M, N, K, A, lda, B, ldb, R, ldr, 0, nthreads);
+}
+
+/* Receiving side of GEMM+RS / GEMM+AR: R = D0 + sum_p A_p B_p.  D0 is the binary32 destination
+   as it stood before the producers added into it (MxN, leading dimension ldd); producer p has
+   A_p (M x K_p, lda_p) and B_p (K_p x N, ldb_p).  Producers are added in index order, each
+   product in ascending k, all in binary64. */
+int pk_oracle_reduce(int64_t M, int64_t N, int num_producers, const int64_t* K,
+                     const uint16_t* const* A, const int64_t* lda,
+                     const uint16_t* const* B, const int64_t* ldb,
+                     const float* D0, int64_t ldd, double* R, int64_t ldr, int nthreads) {
+    if (M < 0 || N < 0 || num_producers < 0) return 1;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            R[i * ldr + j] = D0 ? (double)D0[i * ldd + j] : 0.0;
+    for (int p = 0; p < num_producers; ++p) {
+        int rc = run_gemm(M, N, K[p], A[p], lda[p], B[p], ldb[p], R, ldr, 1, nthreads);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Token dispatch (expert parallelism)                                                          */
+/* ------------------------------------------------------------------------------------------ */
+
+/* For the local experts [expert_begin, expert_begin + num_local): walk the flat routing slots
+   f = t*top_k + k in ascending order and append f to its expert's bucket (a stable counting sort
+   by expert id).  counts[e] = bucket size, offsets = exclusive prefix sum (num_local+1 entries),
+   perm = buckets concatenated in expert order.  Slots routed elsewhere (including ids outside
+   [0, num_experts)) are not local.  Returns the number of local rows, or -1 on bad arguments. */
+int64_t pk_oracle_dispatch(int64_t T, int top_k, const int32_t* topk_ids, int num_experts,
+                           int expert_begin, int num_local,
+                           int32_t* counts, int32_t* offsets, int32_t* perm) {
+    if (T < 0 || top_k < 0 || num_local < 0) return -1;
+    for (int e = 0; e < num_local; ++e) counts[e] = 0;
+    int64_t slots = T * (int64_t)top_k;
+    for (int64_t f = 0; f < slots; ++f) {
+        int32_t id = topk_ids[f];
+        if (id < 0 || id >= num_experts) continue;
+        if (id >= expert_begin && id < expert_begin + num_local) counts[id - expert_begin] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < num_local; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    /* second pass: place each slot at the next free position of its bucket */
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)(num_local > 0 ? num_local : 1));
+    for (int e = 0; e < num_local; ++e) cursor[e] = offsets[e];
+    for (int64_t f = 0; f < slots; ++f) {
+        int32_t id = topk_ids[f];
+        if (id < 0 || id >= num_experts) continue;
+        if (id >= expert_begin && id < expert_begin + num_local)
+            perm[cursor[id - expert_begin]++] = (int32_t)f;
+    }
+    free(cursor);
+    return num_local > 0 ? offsets[num_local] : 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Grouped expert product                                                                       */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Y[j, :] = X[perm[j] / top_k, :] . W_e  for offsets[e] <= j < offsets[e+1], e in [0, num_local).
+   X is tokens x K bf16 (leading dimension ldx); W is num_local consecutive K x N bf16 matrices;
+   Y is rows x N binary64 (leading dimension ldy).  Each row is one plain product in ascending k.
+   The gathered rows of X are copied out first (the gather), then multiplied. */
+int pk_oracle_grouped_gemm(int num_local, const int32_t* offsets, const int32_t* perm, int top_k,
+                           const uint16_t* X, int64_t ldx, int64_t K,
+                           const uint16_t* W, int64_t N, double* Y, int64_t ldy, int nthreads) {
+    if (num_local < 0 || top_k <= 0 || K < 0 || N < 0) return 1;
+    for (int e = 0; e < num_local; ++e) {
+        int64_t r0 = offsets[e], rows = offsets[e + 1] - offsets[e];
+        if (rows <= 0 || N == 0) continue;
+        uint16_t* Ag = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(rows * (K > 0 ? K : 1)));
+        if (!Ag) return 2;
+        for (int64_t j = 0; j < rows; ++j) {
+            int64_t token = perm[r0 + j] / top_k;
+            memcpy(Ag + j * K, X + token * ldx, sizeof(uint16_t) * (size_t)K);
+        }
+        int rc = run_gemm(rows, N, K, Ag, K, W + (int64_t)e * K * N, N, Y + r0 * ldy, ldy, 0,
+                          nthreads);
+        free(Ag);
+        if (rc) return rc;
+    }
+    return 0;
+}

@@ -1,0 +1,75 @@
+"""Comparison helpers for parity checks (test infrastructure).
+
+Tolerances: fp32 results must satisfy relative Frobenius error <= 1e-3 and max abs error
+<= 1e-2 * RMS(reference) against the binary64 oracle, and additionally every element must lie
+within the elementwise error bound of a K-term sum carried out in binary32 (Higham's bound
+gamma_K * sum|a||b| with gamma_K = K u / (1 - K u); u = 2^-23 also covers truncating adders).
+bf16 results are checked against the oracle's correctly rounded value: relative Frobenius error
+<= 1e-3 and each element within one bf16 ulp of the binary64 value plus the binary32 sum bound.
+"""
+import numpy as np
+
+REL_F_TOL = 1e-3
+MAXABS_RMS_TOL = 1e-2
+U32 = 2.0 ** -23
+
+
+def bf16_bits_to_f64(bits):
+    """Exact value of bf16 bit patterns via numpy's binary32 view (no oracle code)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def metrics(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = got - ref
+    nref = np.linalg.norm(ref)
+    relF = float(np.linalg.norm(diff) / nref) if nref > 0 else float(np.linalg.norm(diff))
+    maxabs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    return relF, maxabs, rms
+
+
+def gamma(K):
+    ku = K * U32
+    return ku / (1.0 - ku)
+
+
+def check_f32(got, ref, absprod=None, K=None, what=""):
+    """fp32 output vs binary64 reference: global tolerances + per-element sum bound."""
+    relF, maxabs, rms = metrics(got, ref)
+    assert relF <= REL_F_TOL, "%s relF %.3e" % (what, relF)
+    assert maxabs <= MAXABS_RMS_TOL * rms or maxabs == 0.0, "%s maxabs %.3e rms %.3e" % (what, maxabs, rms)
+    if absprod is not None:
+        bound = gamma(K) * np.asarray(absprod) + 2.0 ** -24 * np.abs(ref) + 1e-30
+        excess = np.abs(np.asarray(got, np.float64) - ref) - bound
+        bad = np.argwhere(excess > 0)
+        assert bad.size == 0, "%s: %d elements outside the binary32 sum bound, first %s" % (
+            what, bad.shape[0], bad[:5].tolist())
+    return relF, maxabs, rms
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 values at |x| (2^(e-7), with the subnormal floor 2^-133)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, -126)
+    return np.where(ax > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def check_bf16(got_bits, ref, ref_rounded_bits, absprod=None, K=None, what=""):
+    """bf16 output vs binary64 reference R and its correctly rounded bits RNE(R)."""
+    got = bf16_bits_to_f64(got_bits)
+    rr = bf16_bits_to_f64(ref_rounded_bits)
+    relF, maxabs, rms = metrics(got, rr)
+    assert relF <= REL_F_TOL, "%s relF vs RNE(R) %.3e" % (what, relF)
+    slack = bf16_ulp(ref)
+    if absprod is not None:
+        slack = slack + gamma(K) * np.asarray(absprod)
+    excess = np.abs(got - np.asarray(ref, np.float64)) - slack
+    bad = np.argwhere(excess > 0)
+    assert bad.size == 0, "%s: %d elements more than one bf16 ulp from R, first %s" % (
+        what, bad.shape[0], bad[:5].tolist())
+    return metrics(got, ref)

@@ -1,0 +1,382 @@
+"""Pins of the oracle: each function checks one property that the pages or the mathematics fix,
+against something other than the oracle itself (hand-worked fixtures, closed forms, exact
+integer or rational arithmetic, an independent library routine, invariants).  Each takes an
+``oracle.Oracle`` and raises AssertionError when the property fails, so the same checks can be
+run against copies of the oracle with a planted mistake (tests/test_oracle_mutants.py).
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import pk_inputs
+from _parity import bf16_bits_to_f64
+
+GOLDEN_DIR = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits(values):
+    return pk_inputs.f32_to_bf16_bits(np.asarray(values, dtype=np.float32))
+
+
+# ------------------------------------------------------------------------------------------- #
+# bf16 rounding (store epilogue, cast pass)                                                     #
+# ------------------------------------------------------------------------------------------- #
+
+def golden_bf16_rows():
+    rows = []
+    for line in open(os.path.join(GOLDEN_DIR, "bf16_rne.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        parts = line.split()
+        x = float(parts[0]) if parts[0] in ("inf", "-inf") else float.fromhex(parts[0])
+        rows.append((x, int(parts[1], 16), " ".join(parts[2:])))
+    return rows
+
+
+def pin_bf16_golden(o):
+    rows = golden_bf16_rows()
+    assert len(rows) >= 20
+    got = o.round_bf16(np.array([r[0] for r in rows]))
+    for (x, want, why), g in zip(rows, got.tolist()):
+        assert g == want, "%r: got %#06x want %#06x (%s)" % (x, g, want, why)
+
+
+def pin_bf16_fixed_points(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bf16_bits_to_f64(bits)
+    keep = np.isfinite(vals)
+    assert np.array_equal(o.round_bf16(vals[keep]), bits[keep])
+
+
+def pin_bf16_midpoints(o):
+    """Between adjacent positive finite bf16 values: the exact midpoint goes to the neighbour
+    with an even fraction; points a quarter-gap either side go to the nearer one."""
+    pos = np.arange(0x0000, 0x7F7F, dtype=np.uint32).astype(np.uint16)
+    lo = bf16_bits_to_f64(pos)
+    hi = bf16_bits_to_f64(pos + 1)
+    mid = (lo + hi) / 2.0
+    q1 = lo + (hi - lo) / 4.0
+    q3 = lo + 3.0 * (hi - lo) / 4.0
+    even = np.where(pos % 2 == 0, pos, pos + 1).astype(np.int64)
+    assert np.array_equal(o.round_bf16(mid).astype(np.int64), even)
+    assert np.array_equal(o.round_bf16(q1).astype(np.int64), pos.astype(np.int64))
+    assert np.array_equal(o.round_bf16(q3).astype(np.int64), pos.astype(np.int64) + 1)
+    assert np.array_equal(o.round_bf16(-mid).astype(np.int64), even | 0x8000)
+
+
+def pin_bf16_matches_torch(o):
+    """Independent library: torch's binary32 -> bfloat16 conversion (round to nearest even)."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    u = rng.integers(0, 2 ** 32, size=100000, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.cast_f32_bf16(x), want)
+    assert np.array_equal(o.round_bf16(x.astype(np.float64)), want)
+
+
+def pin_bf16_decode(o):
+    """Decode equals numpy's binary32 reinterpretation of (h << 16) on a spread of patterns."""
+    sample = np.concatenate([np.arange(0, 65536, 97), [0x7F7F, 0x0001, 0x8001, 0xFF7F, 0x3F80]])
+    sample = sample.astype(np.uint16)
+    want = bf16_bits_to_f64(sample)
+    got = o.bf16_to_f64(sample)
+    fin = np.isfinite(want)
+    assert np.array_equal(got[fin], want[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+
+
+BF16_PINS = [pin_bf16_golden, pin_bf16_fixed_points, pin_bf16_midpoints, pin_bf16_matches_torch,
+             pin_bf16_decode]
+
+
+# ------------------------------------------------------------------------------------------- #
+# products                                                                                      #
+# ------------------------------------------------------------------------------------------- #
+
+def pin_gemm_golden(o):
+    rows = [l.split() for l in open(os.path.join(GOLDEN_DIR, "gemm_small.txt"))
+            if l.strip() and not l.startswith("#")]
+    A = np.array([[float(v) for v in r] for r in rows[0:2]])
+    B = np.array([[float(v) for v in r] for r in rows[2:5]])
+    R = np.array([[float(v) for v in r] for r in rows[5:7]])
+    assert np.array_equal(o.gemm(_bits(A), _bits(B), nthreads=1), R)
+
+
+def pin_gemm_all_ones(o):
+    for M, N, K in [(5, 7, 64), (33, 17, 1024), (3, 130, 8192)]:
+        got = o.gemm(_bits(np.ones((M, K))), _bits(np.ones((K, N))))
+        assert np.array_equal(got, np.full((M, N), float(K))), (M, N, K)
+
+
+def pin_gemm_identity(o):
+    K, N = 96, 40
+    B = pk_inputs.normal_bf16((K, N), 1.0, 11)
+    got = o.gemm(_bits(np.eye(K)), B)
+    assert np.array_equal(got, bf16_bits_to_f64(B))
+    assert np.array_equal(o.round_bf16(got), B)
+
+
+def pin_gemm_rank_one(o):
+    """Only column 0 of A and row 0 of B are non-zero: R = u v^T exactly (distinct M, N, K)."""
+    M, N, K = 37, 23, 48
+    u = pk_inputs.normal_bf16((M,), 1.0, 3)
+    v = pk_inputs.normal_bf16((N,), 1.0, 4)
+    A = np.zeros((M, K), dtype=np.uint16); A[:, 0] = u
+    B = np.zeros((K, N), dtype=np.uint16); B[0, :] = v
+    want = np.outer(bf16_bits_to_f64(u), bf16_bits_to_f64(v))
+    assert np.array_equal(o.gemm(A, B), want)
+
+
+def pin_gemm_small_integers(o):
+    """|a|,|b| <= 4, K = 512: every partial sum is an exact integer, so the binary64 result must
+    equal numpy's int64 product."""
+    M, N, K = 45, 61, 512
+    A = pk_inputs.small_int_bf16((M, K), -4, 4, 21)
+    B = pk_inputs.small_int_bf16((K, N), -4, 4, 22)
+    Ai = bf16_bits_to_f64(A).astype(np.int64)
+    Bi = bf16_bits_to_f64(B).astype(np.int64)
+    assert np.array_equal(o.gemm(A, B), (Ai @ Bi).astype(np.float64))
+
+
+def pin_gemm_brute_force_rational(o):
+    """Exact rational brute force on tiny shapes: the binary64 sum lies within
+    K * 2^-53 * sum|a b| of the exact value."""
+    for M, N, K in [(1, 1, 1), (2, 3, 5), (4, 1, 7), (3, 4, 2)]:
+        A = pk_inputs.normal_bf16((M, K), 1.0, 100 + M)
+        B = pk_inputs.normal_bf16((K, N), 1.0, 200 + N)
+        a = bf16_bits_to_f64(A); b = bf16_bits_to_f64(B)
+        got = o.gemm(A, B, nthreads=1)
+        for i in range(M):
+            for j in range(N):
+                exact = sum(Fraction(a[i, k]) * Fraction(b[k, j]) for k in range(K))
+                absum = sum(abs(a[i, k] * b[k, j]) for k in range(K))
+                assert abs(Fraction(got[i, j]) - exact) <= Fraction(K * 2.0 ** -53 * absum)
+
+
+def pin_gemm_numpy(o):
+    """Independent library product over the same decoded inputs (mid size)."""
+    M, N, K = 96, 80, 1024
+    A = pk_inputs.normal_bf16((M, K), 0.02, 31)
+    B = pk_inputs.normal_bf16((K, N), 0.02, 32)
+    a, b = bf16_bits_to_f64(A), bf16_bits_to_f64(B)
+    got = o.gemm(A, B)
+    assert np.all(np.abs(got - a @ b) <= 2 * K * 2.0 ** -53 * (np.abs(a) @ np.abs(b)))
+
+
+GEMM_PINS = [pin_gemm_golden, pin_gemm_all_ones, pin_gemm_identity, pin_gemm_rank_one,
+             pin_gemm_small_integers, pin_gemm_brute_force_rational, pin_gemm_numpy]
+
+
+# ------------------------------------------------------------------------------------------- #
+# reduction into the destination (GEMM+RS / GEMM+AR receiving side)                             #
+# ------------------------------------------------------------------------------------------- #
+
+def pin_reduce_integer_producers(o):
+    """8 producers with small-integer operands and an integer D0: the sum is exact, so it must
+    equal numpy's int64 arithmetic whatever the order."""
+    M, N, K = 40, 56, 64
+    prods = [(pk_inputs.small_int_bf16((M, K), -3, 3, 300 + p),
+              pk_inputs.small_int_bf16((K, N), -3, 3, 400 + p)) for p in range(8)]
+    D0 = np.random.Generator(np.random.PCG64(9)).integers(-100, 100, size=(M, N)).astype(np.float32)
+    want = D0.astype(np.int64)
+    for a, b in prods:
+        want = want + bf16_bits_to_f64(a).astype(np.int64) @ bf16_bits_to_f64(b).astype(np.int64)
+    assert np.array_equal(o.reduce(D0, prods), want.astype(np.float64))
+
+
+def pin_reduce_all_ones(o):
+    """8 all-ones producers with K = 64 into a zero destination give 512 everywhere."""
+    M, N, K = 16, 24, 64
+    one_a, one_b = _bits(np.ones((M, K))), _bits(np.ones((K, N)))
+    assert np.array_equal(o.reduce(None, [(one_a, one_b)] * 8), np.full((M, N), 512.0))
+
+
+def pin_reduce_concat_identity(o):
+    """sum_p A_p B_p equals one product over the K-concatenated operands (library check)."""
+    M, N, K = 32, 48, 64
+    prods = [(pk_inputs.normal_bf16((M, K), 1.0, 500 + p),
+              pk_inputs.normal_bf16((K, N), 1.0, 600 + p)) for p in range(8)]
+    Acat = np.concatenate([bf16_bits_to_f64(a) for a, _ in prods], axis=1)
+    Bcat = np.concatenate([bf16_bits_to_f64(b) for _, b in prods], axis=0)
+    want = Acat @ Bcat
+    got = o.reduce(None, prods)
+    assert np.all(np.abs(got - want) <= 4 * 512 * 2.0 ** -53 * (np.abs(Acat) @ np.abs(Bcat)))
+
+
+def pin_reduce_keeps_destination(o):
+    """With one producer the result is D0 plus that product; with a zero product it is D0."""
+    M, N, K = 12, 20, 32
+    D0 = np.random.Generator(np.random.PCG64(10)).standard_normal((M, N)).astype(np.float32)
+    zero_a = np.zeros((M, K), dtype=np.uint16)
+    B = pk_inputs.normal_bf16((K, N), 1.0, 12)
+    assert np.array_equal(o.reduce(D0, [(zero_a, B)]), D0.astype(np.float64))
+    A = pk_inputs.small_int_bf16((M, K), -2, 2, 13)
+    Bi = pk_inputs.small_int_bf16((K, N), -2, 2, 14)
+    Di = np.round(D0 * 8).astype(np.float32)
+    want = Di.astype(np.float64) + bf16_bits_to_f64(A) @ bf16_bits_to_f64(Bi)
+    assert np.array_equal(o.reduce(Di, [(A, Bi)]), want)
+
+
+REDUCE_PINS = [pin_reduce_integer_producers, pin_reduce_all_ones, pin_reduce_concat_identity,
+               pin_reduce_keeps_destination]
+
+
+# ------------------------------------------------------------------------------------------- #
+# dispatch                                                                                      #
+# ------------------------------------------------------------------------------------------- #
+
+def golden_dispatch():
+    vals = {}
+    for line in open(os.path.join(GOLDEN_DIR, "dispatch_small.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        k, *v = line.split()
+        vals[k] = [int(x) for x in v]
+    return vals
+
+
+def pin_dispatch_golden(o):
+    g = golden_dispatch()
+    ids = np.array(g["ids"], dtype=np.int32).reshape(g["T"][0], g["top_k"][0])
+    counts, offsets, perm = o.dispatch(ids, g["num_experts"][0], g["expert_begin"][0],
+                                       g["num_local"][0])
+    assert counts.tolist() == g["counts"]
+    assert offsets.tolist() == g["offsets"]
+    assert perm.tolist() == g["perm"]
+
+
+def library_dispatch(ids, num_experts, expert_begin, num_local):
+    """Same result with numpy only: mask local slots, stable argsort by expert id."""
+    flat = np.asarray(ids).reshape(-1).astype(np.int64)
+    valid = (flat >= 0) & (flat < num_experts)
+    local = valid & (flat >= expert_begin) & (flat < expert_begin + num_local)
+    slots = np.nonzero(local)[0]
+    e = flat[slots] - expert_begin
+    order = np.argsort(e, kind="stable")
+    counts = np.bincount(e, minlength=num_local)[:num_local]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    return counts, offsets, slots[order]
+
+
+def pin_dispatch_library(o):
+    for seed, (T, top_k, E, begin, nl) in enumerate([(4096, 8, 256, 0, 32), (1000, 4, 64, 16, 16),
+                                                       (333, 2, 8, 5, 3), (50, 6, 300, 290, 10)]):
+        ids = pk_inputs.zipf_topk(T, E, top_k, 1.1, 70 + seed)
+        c, off, perm = o.dispatch(ids, E, begin, nl)
+        wc, woff, wperm = library_dispatch(ids, E, begin, nl)
+        assert np.array_equal(c, wc) and np.array_equal(off, woff) and np.array_equal(perm, wperm)
+
+
+def pin_dispatch_invariants(o):
+    T, top_k, E, begin, nl = 777, 8, 64, 8, 24
+    ids = pk_inputs.zipf_topk(T, E, top_k, 0.7, 81)
+    c, off, perm = o.dispatch(ids, E, begin, nl)
+    flat = ids.reshape(-1)
+    assert off[0] == 0 and np.all(np.diff(off) >= 0) and np.array_equal(np.diff(off), c)
+    local = np.nonzero((flat >= begin) & (flat < begin + nl))[0]
+    assert off[-1] == local.size == perm.size
+    assert np.array_equal(np.sort(perm), local)          # a bijection onto the local slots
+    for e in range(nl):
+        seg = perm[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)                   # stable: ascending slots
+        assert np.all(flat[seg] == begin + e)             # every slot routed to this expert
+
+
+def pin_dispatch_special_cases(o):
+    # no local tokens
+    ids = np.full((10, 2), 7, dtype=np.int32)
+    c, off, perm = o.dispatch(ids, 8, 0, 4)
+    assert c.tolist() == [0, 0, 0, 0] and off.tolist() == [0] * 5 and perm.size == 0
+    # a single token
+    c, off, perm = o.dispatch(np.array([[1, 3]], dtype=np.int32), 4, 0, 4)
+    assert c.tolist() == [0, 1, 0, 1] and off.tolist() == [0, 0, 1, 1, 2] and perm.tolist() == [0, 1]
+    # every token to one expert (top_k = 1)
+    ids = np.full((9, 1), 2, dtype=np.int32)
+    c, off, perm = o.dispatch(ids, 4, 0, 4)
+    assert c.tolist() == [0, 0, 9, 0] and perm.tolist() == list(range(9))
+    # ids outside [0, num_experts) are never local, even inside the local window
+    ids = np.array([[4, 5], [2, -1], [3, 2]], dtype=np.int32)
+    c, off, perm = o.dispatch(ids, 4, 2, 4)
+    assert c.tolist() == [2, 1, 0, 0] and perm.tolist() == [2, 5, 4]
+
+
+DISPATCH_PINS = [pin_dispatch_golden, pin_dispatch_library, pin_dispatch_invariants,
+                 pin_dispatch_special_cases]
+
+
+# ------------------------------------------------------------------------------------------- #
+# grouped expert product                                                                        #
+# ------------------------------------------------------------------------------------------- #
+
+def pin_grouped_selection_weights(o):
+    """W_e[k, n] = 2^(e mod 8 - 4) if k == n + c_e else 0, with X[t, k] = (t + 1) * 2^(k mod 8 - 4)
+    (at most 6 significant bits, exact in bf16): Y[j, n] = 2^(e mod 8 - 4) * X[perm[j] // top_k,
+    n + c_e] exactly.  Token, column shift and expert scale are all recoverable from Y, so this
+    pins gather, offsets and the expert choice through the product."""
+    T, top_k, E, nl, K, N = 40, 3, 12, 6, 64, 16
+    ids = pk_inputs.zipf_topk(T, E, top_k, 0.5, 91)
+    c, off, perm = o.dispatch(ids, E, 0, nl)
+    tt = np.arange(T)[:, None].astype(np.float64)
+    kk = np.arange(K)[None, :].astype(np.float64)
+    Xv = (tt + 1.0) * 2.0 ** (kk % 8 - 4)
+    X = _bits(Xv)
+    assert np.array_equal(bf16_bits_to_f64(X), Xv)
+    W = np.zeros((nl, K, N), dtype=np.float64)
+    shift = [(3 * e) % (K - N + 1) for e in range(nl)]
+    for e in range(nl):
+        for n in range(N):
+            W[e, n + shift[e], n] = 2.0 ** (e % 8 - 4)
+    Y = o.grouped_gemm(off, perm, top_k, X, _bits(W))
+    for e in range(nl):
+        for j in range(off[e], off[e + 1]):
+            t = perm[j] // top_k
+            want = 2.0 ** (e % 8 - 4) * Xv[t, shift[e]:shift[e] + N]
+            assert np.array_equal(Y[j], want), (e, j)
+
+
+def pin_grouped_one_expert_is_gemm(o):
+    """One local expert, top_k = 1, every token routed to it: the grouped product is the plain
+    product of X with W_0 (rows in token order); checked with the library product."""
+    T, K, N = 50, 96, 24
+    ids = np.zeros((T, 1), dtype=np.int32)
+    c, off, perm = o.dispatch(ids, 1, 0, 1)
+    assert perm.tolist() == list(range(T))
+    X = pk_inputs.normal_bf16((T, K), 1.0, 95)
+    W = pk_inputs.normal_bf16((1, K, N), 0.02, 96)
+    Y = o.grouped_gemm(off, perm, 1, X, W)
+    x, w = bf16_bits_to_f64(X), bf16_bits_to_f64(W[0])
+    assert np.all(np.abs(Y - x @ w) <= 2 * K * 2.0 ** -53 * (np.abs(x) @ np.abs(w)))
+
+
+def pin_grouped_brute_force(o):
+    """Tiny case against exact rationals, row by row, expert by expert."""
+    T, top_k, E, nl, K, N = 6, 2, 5, 3, 5, 3
+    ids = np.array([[0, 2], [1, 0], [2, 4], [0, 1], [3, 2], [1, 2]], dtype=np.int32)
+    c, off, perm = o.dispatch(ids, E, 0, nl)
+    X = pk_inputs.normal_bf16((T, K), 1.0, 97)
+    W = pk_inputs.normal_bf16((nl, K, N), 1.0, 98)
+    x, w = bf16_bits_to_f64(X), bf16_bits_to_f64(W)
+    Y = o.grouped_gemm(off, perm, top_k, X, W)
+    flat = ids.reshape(-1)
+    j = 0
+    for e in range(nl):
+        for f in range(T * top_k):
+            if flat[f] != e:
+                continue
+            t = f // top_k
+            for n in range(N):
+                exact = sum(Fraction(x[t, k]) * Fraction(w[e, k, n]) for k in range(K))
+                absum = sum(abs(x[t, k] * w[e, k, n]) for k in range(K))
+                assert abs(Fraction(Y[j, n]) - exact) <= Fraction(K * 2.0 ** -53 * absum)
+            j += 1
+    assert j == Y.shape[0]
+
+
+GROUPED_PINS = [pin_grouped_selection_weights, pin_grouped_one_expert_is_gemm,
+                pin_grouped_brute_force]
+
+ALL_PINS = BF16_PINS + GEMM_PINS + REDUCE_PINS + DISPATCH_PINS + GROUPED_PINS
