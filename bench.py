@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the one-GPU GEMM+RS local share at N=8192 on MI355X.
+
+One step = one pass of the hot path over the workload: pk_gemm_reduce of A (8192 x 1024 bf16)
+times B (1024 x 8192 bf16) into an 8192 x 8192 fp32 destination held as 8 row shards of 1024
+rows, pre-filled with 7 other producers' partials (tile schedule, operand staging, MFMA loop and
+the reduction epilogue, all in the HIP kernels).  Inputs are seeded synthetic data resident in
+HBM before the timed region.
+
+Prints ONE JSON line (rank 0): TFLOP/s and the fraction of the bf16 dense MFMA peak, the
+roofline of the dominant kernel (timed with HIP events on the stream it runs on), the atomic
+reduction mode measured beside the owner mode, and the oracle's CPU time on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--mode owner|atomic] [--workload rs_8192|...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gemm_tile_granular_bf16_amd", "csrc", f)
+                  for f in ("pk_gemm.hip", "pk_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, mode: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on the
+    current kernel source (null otherwise)."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = data.get("%s/%s" % (workload, mode))
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="rs_8192",
+                    choices=["rs_8192", "ag_8192", "ar_16384", "moe_dispatch", "rs_tiny"])
+    ap.add_argument("--mode", default="owner", choices=["owner", "atomic"])
+    ap.add_argument("--no-variant", action="store_true", help="skip the other reduce mode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+class Timer:
+    """Per-step HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.pairs = []
+
+    def step(self, fn):
+        t = self.torch
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        fn()
+        e1.record(self.stream)
+        self.pairs.append((e0, e1))
+
+    def kernel_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def setup_workload(name, mode, torch, pk):
+    """Returns (step_fn, flops, algorithmic bytes per launch, bound, description)."""
+    import pk_inputs
+    w = pk_inputs.WORKLOADS[name]
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    mode_id = pk.PK_REDUCE_OWNER if mode == "owner" else pk.PK_REDUCE_ATOMIC
+    if w.kind == "reduce":
+        prods = [pk_inputs.producer_operands(w, p) for p in range(w.producers)]
+        if w.prefill_partials:
+            D0 = pk_inputs.rs_prefill(w.M, w.N, w.prefill_partials, w.prefill_std, w.prefill_seed)
+            D = torch.from_numpy(D0).cuda()
+            del D0
+        else:
+            D = torch.zeros((w.M, w.N), device="cuda")
+        shards = list(D.split(w.M // w.shards))
+        ops = [(dev(a), dev(b)) for a, b in prods]
+        out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda") if w.cast_bf16 else None
+
+        def step():
+            for i, (a, b) in enumerate(ops):
+                pk.gemm_reduce(a, b, shards, mode=mode_id,
+                               out_bf16=out if (out is not None and i == len(ops) - 1) else None)
+        flops = w.flops
+        # A and B once, destination read + written once per producer, cast read + write
+        nbytes = sum(2 * (w.M * w.K + w.K * w.N) + 8 * w.M * w.N for _ in prods)
+        if w.cast_bf16:
+            nbytes += 6 * w.M * w.N
+        desc = {"M": w.M, "N": w.N, "K": w.K, "producers": w.producers, "shards": w.shards,
+                "prefill_partials": w.prefill_partials, "reduce": mode,
+                "cast_bf16": w.cast_bf16}
+        return step, flops, nbytes, desc, (D, ops, out)
+    if w.kind == "gemm":
+        A = pk_inputs.normal_bf16((w.M, w.K), w.std_a, w.seed_a)
+        B = pk_inputs.normal_bf16((w.K, w.N), w.std_b, w.seed_b)
+        rows = w.M // w.chunks
+        chunks = [dev(A[i * rows:(i + 1) * rows]) for i in range(w.chunks)]
+        Bd = dev(B)
+        C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            pk.gemm(chunks, Bd, C, first_chunk=0)
+        nbytes = 2 * (w.M * w.K + w.K * w.N + w.M * w.N)
+        desc = {"M": w.M, "N": w.N, "K": w.K, "chunks": w.chunks, "out": "bf16"}
+        return step, w.flops, nbytes, desc, (chunks, Bd, C)
+    # grouped
+    ids, X, W = pk_inputs.moe_inputs(w)
+    ids_d = torch.from_numpy(ids).cuda()
+    Xd, Wd = dev(X), dev(W)
+    offsets = torch.empty(w.num_local + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(w.tokens * w.top_k, dtype=torch.int32, device="cuda")
+    Y = torch.empty((w.tokens * w.top_k, w.N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(pk.grouped_gemm_workspace_size(w.tokens, w.top_k, w.num_local),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        pk.grouped_gemm(ids_d, Xd, Wd, w.num_experts, w.expert_begin, offsets, perm, Y, ws)
+    step()  # the routed row count (device result) prices the step
+    torch.cuda.synchronize()
+    rows = int(offsets[-1].item())
+    flops = 2.0 * rows * w.K * w.N
+    nbytes = 2 * (w.num_local * w.K * w.N + w.tokens * w.K + rows * w.N)
+    desc = {"tokens": w.tokens, "D": w.K, "D_expert": w.N, "top_k": w.top_k,
+            "experts": w.num_experts, "local_experts": w.num_local, "local_rows": rows}
+    return step, flops, nbytes, desc, (ids_d, Xd, Wd, offsets, perm, Y, ws)
+
+
+def run_gpu(name, mode, steps, warmup, torch, pk):
+    step, flops, nbytes, desc, keep = setup_workload(name, mode, torch, pk)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timer(torch, stream)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        timer.step(step)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = timer.kernel_ms()
+    del keep
+    torch.cuda.empty_cache()
+    return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kms, "flops": flops,
+            "bytes": nbytes, "desc": desc}
+
+
+def cpu_baseline(name, target_s):
+    """The oracle as it stands, on a bounded row sample of the same workload."""
+    import oracle
+    import pk_inputs
+    w = pk_inputs.WORKLOADS[name]
+    threads = oracle.default_threads()
+    o = oracle.default()
+    if w.kind == "grouped":
+        return None
+    A = pk_inputs.normal_bf16((w.M, w.K), w.std_a, w.seed_a)
+    B = pk_inputs.normal_bf16((w.K, w.N), w.std_b, w.seed_b)
+    D0 = np.zeros((1, w.N), np.float32)
+
+    def timed(rows):
+        a = np.ascontiguousarray(A[:rows])
+        t = time.perf_counter()
+        if w.kind == "reduce":
+            o.reduce(np.zeros((rows, w.N), np.float32), [(a, B)], nthreads=threads)
+        else:
+            o.gemm(a, B, nthreads=threads)
+        return time.perf_counter() - t
+
+    probe = min(w.M, 64)
+    dt = timed(probe)
+    rows = int(min(w.M, max(probe, probe * target_s / max(dt, 1e-3))))
+    dt = timed(rows)
+    flops = 2.0 * rows * w.N * w.K
+    del D0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d output rows x all %d columns, K=%d, one producer (%.1f s)"
+                      % (rows, w.M, w.N, w.K, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gemm_tile_granular_bf16_amd as pk
+    pk.library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    name = args.workload
+    res = run_gpu(name, args.mode, args.steps, args.warmup, torch, pk)
+    tflops = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
+    ktflops = res["flops"] / (res["kernel_ms"] * 1e-3) / 1e12
+    intensity = res["flops"] / res["bytes"]
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        achieved = res["bytes"] / (res["kernel_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(ktflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ktflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(name, args.mode)
+    roof["algorithmic_bytes"] = res["bytes"]
+    roof["kernel_ms"] = round(res["kernel_ms"], 5)
+    line = {
+        "metric": "TFLOP/s + % bf16 MFMA peak, GEMM+RS local share N=8192 (1 GPU)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "config": dict({"workload": name}, **res["desc"]),
+        "roofline": roof,
+    }
+    if name.startswith("rs") or name.startswith("ar"):
+        if not args.no_variant:
+            other = "atomic" if args.mode == "owner" else "owner"
+            v = run_gpu(name, other, max(5, args.steps // 2), min(args.warmup, 3), torch, pk)
+            line["variant"] = {"reduce": other, "ms_per_step": round(v["ms_per_step"], 5),
+                               "tflops": round(v["flops"] / (v["ms_per_step"] * 1e-3) / 1e12, 2),
+                               "kernel_ms": round(v["kernel_ms"], 5)}
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(name, args.cpu_seconds)
+        if cb is not None:
+            line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+"""Python binding of the gfx950 ParallelKittens one-GPU library (``libpk.so``).
+
+Argument marshalling only: every step of the path (tile scheduling, operand staging, MFMA loop,
+epilogues, cast, dispatch, grouped product) runs in the HIP kernels behind the C ABI declared in
+``include/pk.h``.  PyTorch supplies device memory and streams; nothing here computes results and
+there is no CPU fallback -- if ``libpk.so`` is missing or cannot be loaded, every call raises.
+
+Names follow the C ABI: ``gemm`` (AG+GEMM local share), ``gemm_reduce`` (GEMM+RS / GEMM+AR
+receiving side, optional bf16 cast), ``grouped_gemm`` (token dispatch + expert GEMM).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+__all__ = [
+    "PK_OK", "PK_ERR_INVALID_ARGUMENT", "PK_ERR_UNSUPPORTED", "PK_ERR_HIP", "PK_BF16", "PK_F32",
+    "PK_REDUCE_ATOMIC", "PK_REDUCE_OWNER", "PK_MAX_PARTS", "PKError", "library", "library_path",
+    "gemm", "gemm_reduce", "grouped_gemm", "grouped_gemm_workspace_size",
+]
+
+PK_OK, PK_ERR_INVALID_ARGUMENT, PK_ERR_UNSUPPORTED, PK_ERR_HIP = 0, 1, 2, 3
+PK_BF16, PK_F32 = 0, 1
+PK_REDUCE_ATOMIC, PK_REDUCE_OWNER = 0, 1
+PK_MAX_PARTS = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpk.so")
+_lib = None
+
+
+class PKError(RuntimeError):
+    """A pk_* call returned a non-zero pk_status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load libpk.so (built in-tree by ``gemm_tile_granular_bf16_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError("libpk.so is not built (%s); run gemm_tile_granular_bf16_amd/build.py"
+                          % library_path)
+    lib = ctypes.CDLL(library_path)
+    i64, i32, p, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.pk_gemm.argtypes = [i64, i64, i64, p, i32, i64, i64, i32, p, i64, p, i64, i32, p]
+    lib.pk_gemm.restype = i32
+    lib.pk_gemm_reduce.argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, i64, i64, i32, p, i64,
+                                   p]
+    lib.pk_gemm_reduce.restype = i32
+    lib.pk_grouped_gemm.argtypes = [i64, i32, p, i32, i32, i32, p, i64, i64, p, i64, p, p, p, i64,
+                                    i32, p, sz, p]
+    lib.pk_grouped_gemm.restype = i32
+    lib.pk_grouped_gemm_workspace_size.argtypes = [i64, i32, i32]
+    lib.pk_grouped_gemm_workspace_size.restype = sz
+    lib.pk_status_string.argtypes = [i32]
+    lib.pk_status_string.restype = ctypes.c_char_p
+    lib.pk_last_error.argtypes = []
+    lib.pk_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != PK_OK:
+        lib = library()
+        raise PKError(status, "%s: %s" % (lib.pk_status_string(status).decode(),
+                                          lib.pk_last_error().decode()))
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _matrix(t: torch.Tensor, dtypes, what: str):
+    """(pointer, leading dimension) of a row-major device matrix."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % what)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (what, t.dtype, dtypes))
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be a 2-D row-major matrix (unit column stride)" % what)
+    return t.data_ptr(), t.stride(0) if t.size(0) > 1 else max(t.size(1), t.stride(0))
+
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def gemm(A: Union[torch.Tensor, Sequence[torch.Tensor]], B: torch.Tensor, C: torch.Tensor,
+         first_chunk: int = 0, stream=None) -> torch.Tensor:
+    """C = A @ B (pk_gemm).  ``A`` is one matrix or a list of equal-height row-chunks (the
+    gathered input, last chunk may be shorter); ``B`` is K x N; ``C`` (bf16 or fp32) is written."""
+    chunks = [A] if isinstance(A, torch.Tensor) else list(A)
+    if not chunks or len(chunks) > PK_MAX_PARTS:
+        raise ValueError("1..%d row-chunks" % PK_MAX_PARTS)
+    ptrs, lds = [], set()
+    for i, a in enumerate(chunks):
+        ptr, ld = _matrix(a, _BF16_LIKE, "A chunk %d" % i)
+        ptrs.append(ptr)
+        lds.add(ld)
+    if len(lds) != 1:
+        raise ValueError("all row-chunks must share one leading dimension")
+    chunk_rows = chunks[0].size(0)
+    M = sum(a.size(0) for a in chunks)
+    K = chunks[0].size(1)
+    bp, ldb = _matrix(B, _BF16_LIKE, "B")
+    cp, ldc = _matrix(C, (torch.bfloat16, torch.float32), "C")
+    if B.size(0) != K or C.size(0) != M or C.size(1) != B.size(1):
+        raise ValueError("shapes: A %dx%d, B %s, C %s" % (M, K, tuple(B.shape), tuple(C.shape)))
+    table = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    _check(library().pk_gemm(M, B.size(1), K, table, len(ptrs), chunk_rows, lds.pop(),
+                             first_chunk, bp, ldb, cp, ldc,
+                             PK_BF16 if C.dtype == torch.bfloat16 else PK_F32,
+                             _stream_handle(stream)))
+    return C
+
+
+def gemm_reduce(A: torch.Tensor, B: torch.Tensor, D: Union[torch.Tensor, Sequence[torch.Tensor]],
+                mode: int = PK_REDUCE_ATOMIC, out_bf16: Optional[torch.Tensor] = None,
+                stream=None):
+    """D += A @ B (pk_gemm_reduce).  ``D`` is one fp32 matrix or a list of fp32 row shards of
+    equal height (last may be shorter); ``out_bf16`` (optional) receives the bf16 cast of D."""
+    shards = [D] if isinstance(D, torch.Tensor) else list(D)
+    if not shards or len(shards) > PK_MAX_PARTS:
+        raise ValueError("1..%d destination shards" % PK_MAX_PARTS)
+    ap, lda = _matrix(A, _BF16_LIKE, "A")
+    bp, ldb = _matrix(B, _BF16_LIKE, "B")
+    ptrs, lds = [], set()
+    for i, d in enumerate(shards):
+        ptr, ld = _matrix(d, (torch.float32,), "D shard %d" % i)
+        ptrs.append(ptr)
+        lds.add(ld)
+    if len(lds) != 1:
+        raise ValueError("all destination shards must share one leading dimension")
+    M, K = A.shape
+    N = B.size(1)
+    if B.size(0) != K or sum(d.size(0) for d in shards) != M or any(d.size(1) != N for d in shards):
+        raise ValueError("shapes: A %s, B %s, shards %s" % (tuple(A.shape), tuple(B.shape),
+                                                             [tuple(d.shape) for d in shards]))
+    op, ldo = (None, 0)
+    if out_bf16 is not None:
+        op, ldo = _matrix(out_bf16, (torch.bfloat16,), "out_bf16")
+        if tuple(out_bf16.shape) != (M, N):
+            raise ValueError("out_bf16 must be %dx%d" % (M, N))
+    table = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    _check(library().pk_gemm_reduce(M, N, K, ap, lda, bp, ldb, table, len(ptrs),
+                                    shards[0].size(0), lds.pop(), mode, op, ldo,
+                                    _stream_handle(stream)))
+    return D
+
+
+def grouped_gemm_workspace_size(T: int, top_k: int, num_local: int) -> int:
+    return int(library().pk_grouped_gemm_workspace_size(T, top_k, num_local))
+
+
+def grouped_gemm(topk_ids: torch.Tensor, X: torch.Tensor, W: torch.Tensor, num_experts: int,
+                 expert_begin: int, offsets: torch.Tensor, perm: torch.Tensor, Y: torch.Tensor,
+                 workspace: torch.Tensor, stream=None):
+    """Token dispatch + expert GEMM (pk_grouped_gemm).  ``W`` is num_local x K x N; outputs
+    ``offsets`` (num_local+1 int32), ``perm`` (T*top_k int32) and ``Y`` (T*top_k x N) are written
+    on the device."""
+    if topk_ids.dtype != torch.int32 or not topk_ids.is_cuda or topk_ids.dim() != 2 \
+            or not topk_ids.is_contiguous():
+        raise TypeError("topk_ids must be a contiguous int32 T x top_k device tensor")
+    T, top_k = topk_ids.shape
+    xp, ldx = _matrix(X, _BF16_LIKE, "X")
+    if W.dim() != 3 or not W.is_contiguous() or W.dtype not in _BF16_LIKE or not W.is_cuda:
+        raise TypeError("W must be a contiguous num_local x K x N bf16 device tensor")
+    num_local, K, N = W.shape
+    if X.size(1) != K:
+        raise ValueError("X has %d columns, W expects K=%d" % (X.size(1), K))
+    for t, n, what in ((offsets, num_local + 1, "offsets"), (perm, T * top_k, "perm")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+            raise TypeError("%s must be a contiguous int32 device tensor of >= %d entries" % (what, n))
+    yp, ldy = _matrix(Y, (torch.bfloat16, torch.float32), "Y")
+    if Y.size(0) < T * top_k or Y.size(1) != N:
+        raise ValueError("Y must be at least %d x %d" % (T * top_k, N))
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous device tensor")
+    _check(library().pk_grouped_gemm(T, top_k, topk_ids.data_ptr(), num_experts, expert_begin,
+                                     num_local, xp, ldx, K, W.data_ptr(), N, offsets.data_ptr(),
+                                     perm.data_ptr(), yp, ldy,
+                                     PK_BF16 if Y.dtype == torch.bfloat16 else PK_F32,
+                                     workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream_handle(stream)))
+    return offsets, perm, Y

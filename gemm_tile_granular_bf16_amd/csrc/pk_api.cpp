@@ -1,0 +1,242 @@
+// C ABI of the gfx950 library: argument validation, tile-shape choice, launches.
+// Every check runs on the host before anything is enqueued; no HIP API is called for a call that
+// fails validation.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "pk_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pk_status fail(pk_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pk_status ok() {
+    g_last_error[0] = '\0';
+    return PK_OK;
+}
+
+pk_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(PK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile shape for a dense product: big outputs use 256x256 tiles (one workgroup per CU); when that
+// leaves the 256 CUs under two tiles each, 256x128; small problems 128x128.
+pk::TileCfgId pick_store_cfg(int64_t M, int64_t N) {
+    if (ceil_div(M, 256) * ceil_div(N, 256) >= 512) return pk::CFG_256x256;
+    if (ceil_div(M, 256) * ceil_div(N, 128) >= 256) return pk::CFG_256x128;
+    return pk::CFG_128x128;
+}
+
+// Tile shape for the reduction epilogues: two resident workgroups per CU so that one workgroup's
+// destination traffic overlaps the other's MFMAs.
+pk::TileCfgId pick_reduce_cfg(int64_t M, int64_t N) {
+    if (ceil_div(M, 256) * ceil_div(N, 128) >= 256) return pk::CFG_256x128_2WG;
+    return pk::CFG_128x128;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pk_status_string(pk_status s) {
+    switch (s) {
+        case PK_OK: return "PK_OK";
+        case PK_ERR_INVALID_ARGUMENT: return "PK_ERR_INVALID_ARGUMENT";
+        case PK_ERR_UNSUPPORTED: return "PK_ERR_UNSUPPORTED";
+        case PK_ERR_HIP: return "PK_ERR_HIP";
+    }
+    return "PK_UNKNOWN_STATUS";
+}
+
+const char* pk_last_error(void) { return g_last_error; }
+
+pk_status pk_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* const A_chunks[],
+                  int num_chunks, int64_t chunk_rows, int64_t lda, int first_chunk,
+                  const uint16_t* B, int64_t ldb, void* C, int64_t ldc, pk_dtype c_dtype,
+                  void* stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(PK_ERR_INVALID_ARGUMENT, "negative size");
+    if (c_dtype != PK_BF16 && c_dtype != PK_F32) return fail(PK_ERR_INVALID_ARGUMENT, "c_dtype");
+    if (M == 0 || N == 0) return ok();
+    if (!C) return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
+    if (ldc < N) return fail(PK_ERR_INVALID_ARGUMENT, "leading dimension too small");
+    if (c_dtype == PK_BF16 ? ldc % 8 : ldc % 4)
+        return fail(PK_ERR_UNSUPPORTED, "leading dimensions must be 16-byte multiples");
+    if (!aligned16(C)) return fail(PK_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+    const pk::Epi epi = c_dtype == PK_BF16 ? pk::EPI_STORE_BF16 : pk::EPI_STORE_F32;
+    if (K == 0) {
+        // nothing is read: the product is all zeros
+        pk::GemmArgs z{};
+        z.M = M; z.N = N; z.K = 0;
+        z.C = C; z.ldc = ldc;
+        z.num_chunks = 1;
+        z.group_m = 4;
+        return hip_status(pk::launch_gemm(z, pk::CFG_128x128, epi, (hipStream_t)stream),
+                          "pk_gemm launch");
+    }
+    if (!A_chunks || !B) return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
+    if (num_chunks < 1 || num_chunks > PK_MAX_PARTS)
+        return fail(PK_ERR_INVALID_ARGUMENT, "num_chunks %d outside 1..%d", num_chunks, PK_MAX_PARTS);
+    if (chunk_rows < 1 || ceil_div(M, chunk_rows) != num_chunks)
+        return fail(PK_ERR_INVALID_ARGUMENT, "chunks do not cover M exactly");
+    if (first_chunk < 0 || first_chunk >= num_chunks)
+        return fail(PK_ERR_INVALID_ARGUMENT, "first_chunk out of range");
+    if (lda < K || ldb < N) return fail(PK_ERR_INVALID_ARGUMENT, "leading dimension too small");
+    for (int i = 0; i < num_chunks; ++i)
+        if (!A_chunks[i]) return fail(PK_ERR_INVALID_ARGUMENT, "null A chunk %d", i);
+    if (K % 8 || N % 8) return fail(PK_ERR_UNSUPPORTED, "K and N must be multiples of 8");
+    if (lda % 8 || ldb % 8)
+        return fail(PK_ERR_UNSUPPORTED, "leading dimensions must be 16-byte multiples");
+    for (int i = 0; i < num_chunks; ++i)
+        if (!aligned16(A_chunks[i])) return fail(PK_ERR_UNSUPPORTED, "A chunk %d not 16-byte aligned", i);
+    if (!aligned16(B)) return fail(PK_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+
+    pk::GemmArgs a{};
+    a.M = M; a.N = N; a.K = K;
+    for (int i = 0; i < num_chunks; ++i) a.a_ptr[i] = A_chunks[i];
+    a.chunk_rows = chunk_rows;
+    a.num_chunks = num_chunks;
+    a.lda = lda;
+    a.B = B; a.ldb = ldb;
+    a.C = C; a.ldc = ldc;
+    const pk::TileCfgId cfg = pick_store_cfg(M, N);
+    const pk::TileShape t = pk::tile_shape(cfg);
+    const int tiles_m = (int)ceil_div(M, t.bm);
+    a.rot_tile_rows = (int)(((int64_t)first_chunk * chunk_rows) / t.bm) % tiles_m;
+    a.group_m = 4;
+    return hip_status(pk::launch_gemm(a, cfg, epi, (hipStream_t)stream), "pk_gemm launch");
+}
+
+pk_status pk_gemm_reduce(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                         const uint16_t* B, int64_t ldb, float* const D_shards[], int num_shards,
+                         int64_t shard_rows, int64_t ldd, pk_reduce_mode mode,
+                         uint16_t* out_bf16, int64_t ldo, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(PK_ERR_INVALID_ARGUMENT, "negative size");
+    if (mode != PK_REDUCE_ATOMIC && mode != PK_REDUCE_OWNER)
+        return fail(PK_ERR_INVALID_ARGUMENT, "reduce mode");
+    if (M == 0 || N == 0) return ok();
+    if (!D_shards || (K > 0 && (!A || !B))) return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
+    if (num_shards < 1 || num_shards > PK_MAX_PARTS)
+        return fail(PK_ERR_INVALID_ARGUMENT, "num_shards %d outside 1..%d", num_shards, PK_MAX_PARTS);
+    if (shard_rows < 1 || ceil_div(M, shard_rows) != num_shards)
+        return fail(PK_ERR_INVALID_ARGUMENT, "shards do not cover M exactly");
+    if ((K > 0 && (lda < K || ldb < N)) || ldd < N)
+        return fail(PK_ERR_INVALID_ARGUMENT, "leading dimension too small");
+    if (out_bf16 && ldo < N) return fail(PK_ERR_INVALID_ARGUMENT, "ldo too small");
+    for (int i = 0; i < num_shards; ++i)
+        if (!D_shards[i]) return fail(PK_ERR_INVALID_ARGUMENT, "null destination shard %d", i);
+    if (num_shards > 1 && shard_rows % 32)
+        return fail(PK_ERR_UNSUPPORTED, "with several shards, shard_rows must be a multiple of 32");
+    if (K % 8 || N % 8) return fail(PK_ERR_UNSUPPORTED, "K and N must be multiples of 8");
+    if ((K > 0 && (lda % 8 || ldb % 8)) || ldd % 4 || (out_bf16 && ldo % 8))
+        return fail(PK_ERR_UNSUPPORTED, "leading dimensions must be 16-byte multiples");
+    if ((K > 0 && (!aligned16(A) || !aligned16(B))) || (out_bf16 && !aligned16(out_bf16)))
+        return fail(PK_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+    for (int i = 0; i < num_shards; ++i)
+        if (!aligned16(D_shards[i])) return fail(PK_ERR_UNSUPPORTED, "shard %d not 16-byte aligned", i);
+
+    hipStream_t s = (hipStream_t)stream;
+    if (K > 0) {
+        pk::GemmArgs a{};
+        a.M = M; a.N = N; a.K = K;
+        a.a_ptr[0] = A;
+        a.chunk_rows = M;
+        a.num_chunks = 1;
+        a.lda = lda;
+        a.B = B; a.ldb = ldb;
+        for (int i = 0; i < num_shards; ++i) a.d_ptr[i] = D_shards[i];
+        a.shard_rows = shard_rows;
+        a.num_shards = num_shards;
+        a.ldd = ldd;
+        a.group_m = 8;
+        const pk::Epi epi = mode == PK_REDUCE_ATOMIC ? pk::EPI_ATOMIC_F32 : pk::EPI_OWNER_F32;
+        pk_status st = hip_status(pk::launch_gemm(a, pick_reduce_cfg(M, N), epi, s),
+                                  "pk_gemm_reduce launch");
+        if (st != PK_OK) return st;
+    }
+    if (out_bf16)
+        return hip_status(pk::launch_cast(D_shards, num_shards, shard_rows, ldd, M, N, out_bf16,
+                                          ldo, s),
+                          "pk_gemm_reduce cast launch");
+    return ok();
+}
+
+size_t pk_grouped_gemm_workspace_size(int64_t T, int top_k, int num_local) {
+    if (T < 0 || top_k < 1 || top_k > 64 || num_local < 1 || num_local > 1024) return 0;
+    const pk::DispatchPlan plan = pk::plan_dispatch(T, top_k, num_local);
+    return plan.ws_bytes;
+}
+
+pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num_experts,
+                          int expert_begin, int num_local, const uint16_t* X, int64_t ldx,
+                          int64_t K, const uint16_t* W, int64_t N, int32_t* offsets,
+                          int32_t* perm, void* Y, int64_t ldy, pk_dtype y_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (T < 0 || K < 0 || N < 0) return fail(PK_ERR_INVALID_ARGUMENT, "negative size");
+    if (top_k < 1 || top_k > 64) return fail(PK_ERR_INVALID_ARGUMENT, "top_k outside 1..64");
+    if (num_local < 1 || num_local > 1024) return fail(PK_ERR_INVALID_ARGUMENT, "num_local outside 1..1024");
+    if (num_experts < 1 || expert_begin < 0 || (int64_t)expert_begin + num_local > num_experts)
+        return fail(PK_ERR_INVALID_ARGUMENT, "local expert range outside [0, num_experts)");
+    if (y_dtype != PK_BF16 && y_dtype != PK_F32) return fail(PK_ERR_INVALID_ARGUMENT, "y_dtype");
+    if (T * (int64_t)top_k > INT32_MAX) return fail(PK_ERR_UNSUPPORTED, "more than 2^31 routing slots");
+    if (!offsets || !workspace) return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
+    if (T > 0 && (!topk_ids || !perm)) return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
+    if (T > 0 && N > 0 && (!X || !W || !Y)) return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
+    if (ldx < K || ldy < N) return fail(PK_ERR_INVALID_ARGUMENT, "leading dimension too small");
+    const pk::DispatchPlan plan = pk::plan_dispatch(T, top_k, num_local);
+    if (workspace_bytes < plan.ws_bytes)
+        return fail(PK_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, need %zu", workspace_bytes,
+                    plan.ws_bytes);
+    if (K % 8 || N % 8) return fail(PK_ERR_UNSUPPORTED, "K and N must be multiples of 8");
+    if (ldx % 8 || (y_dtype == PK_BF16 ? ldy % 8 : ldy % 4))
+        return fail(PK_ERR_UNSUPPORTED, "leading dimensions must be 16-byte multiples");
+    if ((X && !aligned16(X)) || (W && !aligned16(W)) || (Y && !aligned16(Y)) || !aligned16(workspace))
+        return fail(PK_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+
+    hipStream_t s = (hipStream_t)stream;
+    // workspace: [slice counts | tile offsets]
+    int32_t* slice_counts = (int32_t*)workspace;
+    int32_t* tile_offsets = slice_counts + (size_t)plan.num_slices * num_local;
+    const pk::TileCfgId cfg = pk::CFG_256x256;
+    const pk::TileShape t = pk::tile_shape(cfg);
+    hipError_t e = pk::launch_dispatch(plan, topk_ids, num_experts, expert_begin, num_local, t.bm,
+                                       offsets, perm, tile_offsets, slice_counts, s);
+    if (e != hipSuccess) return hip_status(e, "pk_grouped_gemm dispatch launch");
+    if (T == 0 || N == 0) return ok();
+
+    pk::GemmArgs a{};
+    a.M = T * (int64_t)top_k;
+    a.N = N; a.K = K;
+    a.a_ptr[0] = X;
+    a.num_chunks = 1;
+    a.chunk_rows = 1;
+    a.lda = ldx;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.tile_offsets = tile_offsets;
+    a.top_k = top_k;
+    a.num_local = num_local;
+    a.B = W; a.ldb = N;
+    a.b_stride = K * N;
+    a.C = Y; a.ldc = ldy;
+    // sum_e ceil(count_e / BM) <= rows / BM + num_local, and rows <= T * top_k
+    const int64_t rows_max = T * (int64_t)top_k;
+    const int64_t max_tiles = (rows_max / t.bm + num_local) * ceil_div(N, t.bn);
+    const pk::Epi epi = y_dtype == PK_BF16 ? pk::EPI_STORE_BF16 : pk::EPI_STORE_F32;
+    return hip_status(pk::launch_grouped(a, cfg, epi, max_tiles, s), "pk_grouped_gemm launch");
+}
+
+}  // extern "C"

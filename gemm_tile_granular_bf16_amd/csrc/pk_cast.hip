@@ -1,0 +1,58 @@
+// Cast pass after the all-reduce: fp32 destination -> bf16, round to nearest even
+// ("Loads and Loads of Fluffy Kittens" summary, Results: GEMM+AR; the bf16 output of the reduced
+// tensor).  Pure HBM streaming: each thread moves 8 consecutive elements (two 16-byte loads, one
+// 16-byte store); the grid strides over rows x 8-column groups of every shard.
+#include "pk_internal.h"
+
+namespace pk {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__global__ __launch_bounds__(256) void cast_f32_bf16_kernel(const float* __restrict__ src,
+                                                            int64_t lds_, int64_t rows,
+                                                            int64_t cols8,
+                                                            uint16_t* __restrict__ dst,
+                                                            int64_t ldo) {
+    const int64_t total = rows * cols8;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / cols8, c = (i - r * cols8) * 8;
+        const f32x4 a = *(const f32x4*)(src + r * lds_ + c);
+        const f32x4 b = *(const f32x4*)(src + r * lds_ + c + 4);
+        u32x4 o;
+        o[0] = bf16_rne_bits(a[0]) | (bf16_rne_bits(a[1]) << 16);
+        o[1] = bf16_rne_bits(a[2]) | (bf16_rne_bits(a[3]) << 16);
+        o[2] = bf16_rne_bits(b[0]) | (bf16_rne_bits(b[1]) << 16);
+        o[3] = bf16_rne_bits(b[2]) | (bf16_rne_bits(b[3]) << 16);
+        *(u32x4*)(dst + r * ldo + c) = o;
+    }
+}
+
+hipError_t launch_cast(float* const* d_ptr, int num_shards, int64_t shard_rows, int64_t ldd,
+                       int64_t M, int64_t N, uint16_t* out, int64_t ldo, hipStream_t stream) {
+    for (int s = 0; s < num_shards; ++s) {
+        const int64_t r0 = (int64_t)s * shard_rows;
+        int64_t rows = M - r0;
+        if (rows > shard_rows) rows = shard_rows;
+        if (rows <= 0) break;
+        const int64_t work = rows * (N / 8);
+        int64_t blocks = (work + 255) / 256;
+        if (blocks > 256 * 16) blocks = 256 * 16;
+        if (blocks < 1) blocks = 1;
+        hipLaunchKernelGGL(cast_f32_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const float*)d_ptr[s], ldd, rows, N / 8, out + r0 * ldo, ldo);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace pk

@@ -1,0 +1,182 @@
+// Token dispatch for the expert-parallel path on gfx950.
+//
+// Routed slots f = t*top_k + k are grouped by local expert, stably (ascending f inside an expert)
+// ("Loads and Loads of Fluffy Kittens" summary, Key claims and Results: token-dispatch + GEMM for
+// expert parallelism).  Three small launches on the caller's stream, no host synchronisation:
+//
+//   1. count:   each single-wave workgroup walks one slice of slots, 64 at a time, and counts
+//               slots per expert (lanes that share an expert are found with one ballot per key
+//               bit, so each group adds its size once);
+//   2. scan:    per-expert totals, the exclusive prefix over experts (offsets), each slice's
+//               starting position inside each expert, and the per-expert M-tile prefix that the
+//               grouped product uses as its tile list;
+//   3. scatter: the slices are walked again in the same order; a slot's position is its slice's
+//               base for that expert plus its rank among earlier slots of the same expert.
+//
+// The result is a pure function of topk_ids, so it is bit-exact against any stable grouping.
+#include "pk_internal.h"
+
+namespace pk {
+
+static constexpr int kMaxLocal = 1024;         // experts per rank
+static constexpr int kScanLds = 16384;         // int32 slice-count entries staged in LDS
+
+DispatchPlan plan_dispatch(int64_t T, int top_k, int num_local) {
+    DispatchPlan p{};
+    p.slots = T * (int64_t)top_k;
+    int max_slices = kScanLds / (num_local > 0 ? num_local : 1);
+    if (max_slices > 64) max_slices = 64;
+    if (max_slices < 1) max_slices = 1;
+    int64_t per = (p.slots + max_slices - 1) / max_slices;
+    if (per < 64) per = 64;
+    per = (per + 63) / 64 * 64;
+    p.slice = per;
+    p.num_slices = (int)((p.slots + per - 1) / per);
+    if (p.num_slices < 1) p.num_slices = 1;
+    size_t words = (size_t)p.num_slices * (size_t)num_local + (size_t)num_local + 1;
+    p.ws_bytes = (words * 4 + 255) / 256 * 256;
+    return p;
+}
+
+// Key of slot f: local expert index, or num_local for "not local".
+__device__ __forceinline__ int slot_key(const int32_t* ids, int64_t f, int64_t slots,
+                                        int num_experts, int expert_begin, int num_local) {
+    if (f >= slots) return num_local;
+    const int id = ids[f];
+    if (id < 0 || id >= num_experts) return num_local;
+    const int e = id - expert_begin;
+    return (e >= 0 && e < num_local) ? e : num_local;
+}
+
+// Lanes of the wave holding the same key as this lane.
+__device__ __forceinline__ uint64_t same_key_lanes(int key, int key_bits) {
+    uint64_t m = ~0ull;
+    for (int b = 0; b < key_bits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t ones = __ballot(bit);
+        m &= bit ? ones : ~ones;
+    }
+    return m;
+}
+
+__global__ __launch_bounds__(64) void dispatch_count_kernel(const int32_t* ids, int64_t slots,
+                                                            int64_t slice, int num_experts,
+                                                            int expert_begin, int num_local,
+                                                            int key_bits, int32_t* slice_counts) {
+    __shared__ int cnt[kMaxLocal];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < num_local; e += 64) cnt[e] = 0;
+    __syncthreads();
+    const int64_t f0 = (int64_t)blockIdx.x * slice;
+    for (int64_t base = 0; base < slice; base += 64) {
+        const int64_t f = f0 + base + lane;
+        const int key = slot_key(ids, f, slots, num_experts, expert_begin, num_local);
+        const uint64_t same = same_key_lanes(key, key_bits);
+        const int first = __ffsll((unsigned long long)same) - 1;
+        if (key < num_local && lane == first) cnt[key] += __popcll(same);
+        __syncthreads();
+    }
+    for (int e = lane; e < num_local; e += 64)
+        slice_counts[(int64_t)blockIdx.x * num_local + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int num_slices, int num_local,
+                                                             int tile_m, int32_t* slice_counts,
+                                                             int32_t* offsets,
+                                                             int32_t* tile_offsets) {
+    __shared__ int stage[kScanLds];
+    __shared__ int tot[kMaxLocal];
+    __shared__ int scan_a[kMaxLocal], scan_b[kMaxLocal];
+    const int tid = threadIdx.x;
+    const int n = num_slices * num_local;
+    for (int i = tid; i < n; i += blockDim.x) stage[i] = slice_counts[i];
+    __syncthreads();
+    // running base of every slice inside each expert
+    for (int e = tid; e < num_local; e += blockDim.x) {
+        int run = 0;
+        for (int s = 0; s < num_slices; ++s) {
+            const int c = stage[s * num_local + e];
+            stage[s * num_local + e] = run;
+            run += c;
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    // inclusive scans over experts (Hillis-Steele), of counts and of M-tile counts
+    for (int e = tid; e < num_local; e += blockDim.x) {
+        scan_a[e] = tot[e];
+        scan_b[e] = (tot[e] + tile_m - 1) / tile_m;
+    }
+    __syncthreads();
+    for (int d = 1; d < num_local; d <<= 1) {
+        int va = 0, vb = 0;
+        const bool act = tid < num_local && tid >= d;
+        if (act) { va = scan_a[tid - d]; vb = scan_b[tid - d]; }
+        __syncthreads();
+        if (act) { scan_a[tid] += va; scan_b[tid] += vb; }
+        __syncthreads();
+    }
+    if (tid == 0) { offsets[0] = 0; tile_offsets[0] = 0; }
+    for (int e = tid; e < num_local; e += blockDim.x) {
+        offsets[e + 1] = scan_a[e];
+        tile_offsets[e + 1] = scan_b[e];
+    }
+    // final position of each slice's first slot of expert e
+    for (int i = tid; i < n; i += blockDim.x) {
+        const int e = i % num_local;
+        slice_counts[i] = stage[i] + (scan_a[e] - tot[e]);
+    }
+}
+
+__global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* ids, int64_t slots,
+                                                              int64_t slice, int num_experts,
+                                                              int expert_begin, int num_local,
+                                                              int key_bits,
+                                                              const int32_t* slice_base,
+                                                              int32_t* perm) {
+    __shared__ int run[kMaxLocal];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < num_local; e += 64)
+        run[e] = slice_base[(int64_t)blockIdx.x * num_local + e];
+    __syncthreads();
+    const int64_t f0 = (int64_t)blockIdx.x * slice;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int64_t base = 0; base < slice; base += 64) {
+        const int64_t f = f0 + base + lane;
+        const int key = slot_key(ids, f, slots, num_experts, expert_begin, num_local);
+        const uint64_t same = same_key_lanes(key, key_bits);
+        const int rank = __popcll(same & below);
+        int pos = 0;
+        if (key < num_local) pos = run[key] + rank;
+        __syncthreads();
+        if (key < num_local) {
+            perm[pos] = (int32_t)f;
+            if (rank == 0) run[key] = pos + __popcll(same);
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_dispatch(const DispatchPlan& plan, const int32_t* topk_ids, int num_experts,
+                           int expert_begin, int num_local, int tile_m, int32_t* offsets,
+                           int32_t* perm, int32_t* tile_offsets, int32_t* slice_counts,
+                           hipStream_t stream) {
+    int key_bits = 0;
+    while ((1 << key_bits) <= num_local) ++key_bits;  // keys 0..num_local
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(plan.num_slices), dim3(64), 0, stream,
+                       topk_ids, plan.slots, plan.slice, num_experts, expert_begin, num_local,
+                       key_bits, slice_counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, stream, plan.num_slices,
+                       num_local, tile_m, slice_counts, offsets, tile_offsets);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(plan.num_slices), dim3(64), 0, stream,
+                       topk_ids, plan.slots, plan.slice, num_experts, expert_begin, num_local,
+                       key_bits, slice_counts, perm);
+    return hipGetLastError();
+}
+
+}  // namespace pk

@@ -1,0 +1,85 @@
+// Internal interface between the C-ABI layer (pk_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pk.h"
+
+namespace pk {
+
+// Output-tile epilogues of the tiled GEMM.
+enum Epi : int {
+    EPI_STORE_BF16 = 0,  // C = bf16(acc), round to nearest even
+    EPI_STORE_F32 = 1,   // C = acc
+    EPI_ATOMIC_F32 = 2,  // D += acc, one fp32 atomic add per element
+    EPI_OWNER_F32 = 3    // D += acc, owner-exclusive vector read-modify-write
+};
+
+// Tile shapes compiled into the library (see pk_gemm.hip for what each is used for).
+enum TileCfgId : int {
+    CFG_256x256 = 0,  // 4 waves of 128x128, BK 64, one workgroup per CU
+    CFG_256x128 = 1,  // 4 waves of 128x64, BK 64, one workgroup per CU
+    CFG_256x128_2WG = 2,  // 4 waves of 128x64, BK 32, two workgroups per CU
+    CFG_128x128 = 3,  // 4 waves of 64x64, BK 64
+    CFG_COUNT = 4
+};
+
+struct GemmArgs {
+    int64_t M, N, K;
+    // A rows: row-chunk table (dense) or token rows gathered through perm (grouped)
+    const uint16_t* a_ptr[PK_MAX_PARTS];
+    int64_t chunk_rows;
+    int num_chunks;
+    int64_t lda;
+    int rot_tile_rows;  // chunk-major visiting order: first tile row to visit
+    int group_m;        // tile rows per raster group (L2 locality)
+    // grouped product
+    const int32_t* offsets;       // [num_local + 1]
+    const int32_t* perm;          // [rows]
+    const int32_t* tile_offsets;  // [num_local + 1], M-tiles prefix
+    int top_k;
+    int num_local;
+    // B
+    const uint16_t* B;
+    int64_t ldb;
+    int64_t b_stride;  // elements between consecutive experts' weight matrices
+    // epilogue
+    void* C;
+    int64_t ldc;
+    float* d_ptr[PK_MAX_PARTS];
+    int64_t shard_rows;
+    int num_shards;
+    int64_t ldd;
+};
+
+struct TileShape {
+    int bm, bn;
+};
+TileShape tile_shape(TileCfgId cfg);
+
+// Dense product over a row-chunked A; `epi` selects the epilogue.
+hipError_t launch_gemm(const GemmArgs& a, TileCfgId cfg, Epi epi, hipStream_t stream);
+// Grouped product: tile list read on the device from offsets / tile_offsets; `max_tiles` is an
+// upper bound of the tile count used to size the grid.
+hipError_t launch_grouped(const GemmArgs& a, TileCfgId cfg, Epi epi, int64_t max_tiles,
+                          hipStream_t stream);
+
+// fp32 destination rows [0, M) -> bf16 (round to nearest even), shard by shard.
+hipError_t launch_cast(float* const* d_ptr, int num_shards, int64_t shard_rows, int64_t ldd,
+                       int64_t M, int64_t N, uint16_t* out, int64_t ldo, hipStream_t stream);
+
+// Dispatch: counts, offsets, stable permutation and per-expert M-tile prefix.
+struct DispatchPlan {
+    int64_t slots;      // T * top_k
+    int num_slices;     // workgroups of the count / scatter passes
+    int64_t slice;      // routing slots per workgroup (multiple of 64)
+    size_t ws_bytes;    // workspace needed
+};
+DispatchPlan plan_dispatch(int64_t T, int top_k, int num_local);
+hipError_t launch_dispatch(const DispatchPlan& plan, const int32_t* topk_ids, int num_experts,
+                           int expert_begin, int num_local, int tile_m, int32_t* offsets,
+                           int32_t* perm, int32_t* tile_offsets, int32_t* slice_counts,
+                           hipStream_t stream);
+
+}  // namespace pk

@@ -1,0 +1,160 @@
+/*
+ * pk.h -- C ABI of the MI355X (gfx950) one-GPU share of the ParallelKittens
+ * compute-communication kernels.
+ *
+ * The pages describe three families of fused kernels ("Loads and Loads of Fluffy Kittens"
+ * summary, Key claims and Results; ParallelKittens arXiv abstract): AG+GEMM, GEMM+RS / GEMM+AR
+ * for tensor and data parallelism, and token-dispatch + expert GEMM for expert parallelism.  One
+ * GPU's share of each is a tiled bf16 GEMM whose output tiles go to a fused epilogue.  This header
+ * exposes that share:
+ *
+ *   pk_gemm          -- gathered row-chunks of A times the local B, plain store (AG+GEMM);
+ *   pk_gemm_reduce   -- local product whose output tiles are added into destination shards, with
+ *                       an optional bf16 cast pass (receiving side of GEMM+RS / GEMM+AR);
+ *   pk_grouped_gemm  -- token dispatch (stable grouping of routed slots per local expert) followed
+ *                       by the per-expert product over the gathered rows.
+ *
+ * Conventions shared by every entry point:
+ *   - bf16 values are passed as uint16_t bit patterns (IEEE binary32 upper halves).
+ *   - Every data pointer is a DEVICE pointer on the current HIP device.  Matrices are row-major;
+ *     leading dimensions are in elements.  Inputs must not alias outputs.
+ *   - Ownership: the caller allocates and owns every buffer; the library keeps no pointer after a
+ *     call returns and allocates no device memory.
+ *   - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  No
+ *     entry point synchronises with the host.
+ *   - Errors are returned synchronously, before any launch, as pk_status; nothing is enqueued when
+ *     a call fails.  pk_last_error() gives a human-readable reason for the calling thread's most
+ *     recent failure.  A failing launch returns PK_ERR_HIP; a device fault surfaces at the caller's
+ *     next synchronisation.  No C++ exception crosses this boundary.
+ *   - Shape support: K % 8 == 0 and N % 8 == 0; bf16 leading dimensions % 8 == 0 and fp32 leading
+ *     dimensions % 4 == 0; every pointer 16-byte aligned.  M is arbitrary.  Violations give
+ *     PK_ERR_UNSUPPORTED.  M == 0 or N == 0 is a successful no-op.
+ */
+#ifndef PK_H
+#define PK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pk_status {
+    PK_OK = 0,
+    PK_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, ld < cols, bad table, ... */
+    PK_ERR_UNSUPPORTED = 2,      /* alignment or divisibility outside the supported set */
+    PK_ERR_HIP = 3               /* the HIP runtime rejected a launch */
+} pk_status;
+
+typedef enum pk_dtype {
+    PK_BF16 = 0, /* bf16, round to nearest even from the fp32 accumulator */
+    PK_F32 = 1   /* the fp32 accumulator as is */
+} pk_dtype;
+
+/* How output tiles are added into the destination (pk_gemm_reduce).  Both compute, for every
+   element, fp32(D + acc) with one rounding, so for a single producer they give the same bits. */
+typedef enum pk_reduce_mode {
+    /* One fp32 atomic add per element.  Any number of producers -- other calls on other streams
+       -- may add into the same destination concurrently.  This is the pages' receiving side, where
+       each output tile "is sent and atomically added at the destination". */
+    PK_REDUCE_ATOMIC = 0,
+    /* Owner-exclusive read-modify-write of each output tile with plain vector loads and stores.
+       The caller guarantees that nothing else reads or writes the destination rows of this call
+       while it runs (producers into one destination are serialised, e.g. on one stream).  On
+       gfx950 the atomic unit sustains about a third of the HBM read-modify-write rate, so this is
+       the fast path for a destination with one writer at a time. */
+    PK_REDUCE_OWNER = 1
+} pk_reduce_mode;
+
+/* Row-chunk and shard pointer tables are passed by value, at most this many entries. */
+#define PK_MAX_PARTS 16
+
+/*
+ * pk_gemm -- AG+GEMM local share ("Loads and Loads of Fluffy Kittens" summary, Results: AG+GEMM,
+ * local shape N x N/8 x N; Method: tiles of the gathered input are consumed as they arrive).
+ *
+ *   C[r][c] = sum_k A[r][k] * B[k][c]   for 0 <= r < M, 0 <= c < N, fp32 accumulation.
+ *
+ * A is given as `num_chunks` row-chunks (1..PK_MAX_PARTS): chunk i holds global rows
+ * [i*chunk_rows, min(M, (i+1)*chunk_rows)) at A_chunks[i], leading dimension lda; the chunks must
+ * cover M exactly (num_chunks == ceil(M / chunk_rows)).  Output tiles are visited chunk-major,
+ * starting with chunk `first_chunk` (the rank's own chunk in the multi-GPU setting); the result does
+ * not depend on the order.  B is K x N (ldb).  C is M x N (ldc) of c_dtype (bf16: round to nearest
+ * even).  K == 0 stores zeros.
+ */
+pk_status pk_gemm(int64_t M, int64_t N, int64_t K,
+                  const uint16_t* const A_chunks[], int num_chunks, int64_t chunk_rows,
+                  int64_t lda, int first_chunk,
+                  const uint16_t* B, int64_t ldb,
+                  void* C, int64_t ldc, pk_dtype c_dtype,
+                  void* stream);
+
+/*
+ * pk_gemm_reduce -- GEMM+RS / GEMM+AR receiving side ("Loads and Loads of Fluffy Kittens" summary,
+ * Method: the output tile of the tiled GEMM is exactly what is sent and atomically added at the
+ * destination; Results: GEMM+RS local shape N x N x N/8, GEMM+AR).
+ *
+ *   D[r][c] += sum_k A[r][k] * B[k][c]   for 0 <= r < M, 0 <= c < N (fp32 accumulation, one fp32
+ *   rounding of the addition), where row r lives in shard s = r / shard_rows at
+ *   D_shards[s][(r - s*shard_rows) * ldd + c].
+ *
+ * The shards must cover M exactly (num_shards == ceil(M / shard_rows), 1..PK_MAX_PARTS); with more
+ * than one shard, shard_rows must be a multiple of 32 (PK_ERR_UNSUPPORTED otherwise).  `mode`
+ * selects per-element fp32 atomics or the owner-exclusive read-modify-write (see pk_reduce_mode).
+ * If out_bf16 != NULL, a cast pass follows on the same stream, after this call's reduction:
+ * out_bf16[r*ldo + c] = bf16_round_nearest_even(D[r][c]) for every r < M, c < N (the all-reduce
+ * output; the caller makes sure every other producer has finished by then).  K == 0 adds nothing.
+ */
+pk_status pk_gemm_reduce(int64_t M, int64_t N, int64_t K,
+                         const uint16_t* A, int64_t lda,
+                         const uint16_t* B, int64_t ldb,
+                         float* const D_shards[], int num_shards, int64_t shard_rows, int64_t ldd,
+                         pk_reduce_mode mode,
+                         uint16_t* out_bf16, int64_t ldo,
+                         void* stream);
+
+/*
+ * pk_grouped_gemm -- token dispatch + expert GEMM, one rank's local experts ("Loads and Loads of
+ * Fluffy Kittens" summary, Key claims and Results: token-dispatch + GEMM for expert parallelism,
+ * top_k = 8, 256 experts, D = 7168, D_expert = 2048).
+ *
+ * Dispatch.  topk_ids is T x top_k int32 (device).  Routing slot f = t*top_k + k is local when
+ * expert_begin <= topk_ids[f] < expert_begin + num_local; ids outside [0, num_experts) are never
+ * local (device data cannot be rejected without a host synchronisation, so they are skipped, not
+ * reported).  Outputs, written on the device:
+ *   offsets[num_local + 1]  exclusive prefix sum of per-expert slot counts; offsets[num_local] is
+ *                           the number of local rows;
+ *   perm[T*top_k]           perm[j] = f for the local slots, expert-major and, within an expert,
+ *                           in ascending f (a stable grouping); entries past offsets[num_local]
+ *                           are left untouched.
+ * Product.  For offsets[e] <= j < offsets[e+1]:
+ *   Y[j][c] = sum_k X[perm[j] / top_k][k] * W[e][k][c]
+ * with X T x K (ldx), W num_local consecutive K x N row-major matrices, Y T*top_k x N (ldy, y_dtype;
+ * rows past offsets[num_local] are left untouched).  `workspace` is device scratch of at least
+ * pk_grouped_gemm_workspace_size(T, top_k, num_local) bytes, owned by the caller; its contents
+ * need no initialisation and are meaningless afterwards.  1 <= num_local <= 1024, 1 <= top_k <= 64.
+ */
+pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num_experts,
+                          int expert_begin, int num_local,
+                          const uint16_t* X, int64_t ldx, int64_t K,
+                          const uint16_t* W, int64_t N,
+                          int32_t* offsets, int32_t* perm,
+                          void* Y, int64_t ldy, pk_dtype y_dtype,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Device workspace bytes pk_grouped_gemm needs for this routing shape (0 on invalid sizes). */
+size_t pk_grouped_gemm_workspace_size(int64_t T, int top_k, int num_local);
+
+/* Static description of a status code. */
+const char* pk_status_string(pk_status s);
+
+/* Reason for the calling thread's most recent failing call ("" if none). */
+const char* pk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PK_H */

@@ -1,0 +1,121 @@
+"""The C-ABI library loads and exports every entry point include/pk.h declares, and its host-side
+argument validation rejects bad calls before anything is launched (CPU only: no call here
+passes validation, so no HIP launch is attempted)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pk.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gemm_tile_granular_bf16_amd as pk
+    if not os.path.exists(pk.library_path):
+        from gemm_tile_granular_bf16_amd import build
+        build.build()
+    return pk.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pk_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("pk_gemm", "pk_gemm_reduce", "pk_grouped_gemm", "pk_grouped_gemm_workspace_size",
+              "pk_status_string", "pk_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.pk_status_string(0) == b"PK_OK"
+    assert lib.pk_status_string(1) == b"PK_ERR_INVALID_ARGUMENT"
+    assert lib.pk_status_string(2) == b"PK_ERR_UNSUPPORTED"
+    assert lib.pk_status_string(3) == b"PK_ERR_HIP"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+# The validation tests hand the library fake device addresses.  They are meant for machines
+# without a GPU; where one is visible they are skipped, so that a broken check can never turn
+# into a launch on a bogus address.
+needs_no_gpu = pytest.mark.skipif(
+    os.path.exists("/dev/kfd") and os.environ.get("PK_ABI_FAKE_POINTERS") != "1",
+    reason="fake-pointer validation tests run only where no GPU is visible")
+
+
+def _table(n, base=FAKE):
+    return (ctypes.c_void_p * n)(*[base + 4096 * i for i in range(n)])
+
+
+@needs_no_gpu
+def test_gemm_validation(lib):
+    t = _table(1)
+    # empty problem is a no-op success
+    assert lib.pk_gemm(0, 64, 64, t, 1, 1, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 0
+    assert lib.pk_gemm(64, 0, 64, t, 1, 64, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 0
+    assert lib.pk_gemm(-1, 64, 64, t, 1, 64, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 1
+    assert lib.pk_gemm(64, 64, 64, t, 1, 64, 64, 0, None, 64, FAKE, 64, 0, None) == 1
+    assert lib.pk_gemm(64, 64, 64, t, 1, 64, 64, 0, FAKE, 64, FAKE, 64, 7, None) == 1  # dtype
+    assert lib.pk_gemm(64, 64, 64, t, 0, 64, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 1  # chunks
+    assert lib.pk_gemm(64, 64, 64, _table(17), 17, 4, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 1
+    assert lib.pk_gemm(64, 64, 64, _table(2), 2, 16, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 1  # cover
+    assert lib.pk_gemm(64, 64, 64, _table(2), 2, 32, 64, 2, FAKE, 64, FAKE, 64, 0, None) == 1  # first
+    assert lib.pk_gemm(64, 64, 64, t, 1, 64, 32, 0, FAKE, 64, FAKE, 64, 0, None) == 1  # lda < K
+    assert lib.pk_gemm(64, 64, 60, t, 1, 64, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 2  # K % 8
+    assert lib.pk_gemm(64, 60, 64, t, 1, 64, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 2  # N % 8
+    assert lib.pk_gemm(64, 64, 64, t, 1, 64, 68, 0, FAKE, 64, FAKE, 64, 0, None) == 2  # lda % 8
+    assert lib.pk_gemm(64, 64, 64, _table(1, FAKE + 2), 1, 64, 64, 0, FAKE, 64, FAKE, 64, 0, None) == 2
+    assert b"aligned" in lib.pk_last_error()
+
+
+@needs_no_gpu
+def test_gemm_reduce_validation(lib):
+    d = _table(8)
+    assert lib.pk_gemm_reduce(0, 64, 64, FAKE, 64, FAKE, 64, d, 8, 1, 64, 0, None, 0, None) == 0
+    assert lib.pk_gemm_reduce(64, 64, 64, FAKE, 64, FAKE, 64, d, 8, 8, 64, 5, None, 0, None) == 1
+    assert lib.pk_gemm_reduce(64, 64, 64, FAKE, 64, FAKE, 64, d, 4, 8, 64, 0, None, 0, None) == 1
+    assert lib.pk_gemm_reduce(64, 64, 64, None, 64, FAKE, 64, d, 8, 8, 64, 0, None, 0, None) == 1
+    assert lib.pk_gemm_reduce(64, 64, 64, FAKE, 64, FAKE, 64, d, 2, 32, 32, 0, None, 0, None) == 1
+    # several shards need shard_rows % 32 == 0
+    assert lib.pk_gemm_reduce(64, 64, 64, FAKE, 64, FAKE, 64, d, 8, 8, 64, 0, None, 0, None) == 2
+    assert lib.pk_gemm_reduce(64, 64, 64, FAKE, 64, FAKE, 64, d, 2, 32, 66, 0, None, 0, None) == 2
+    assert lib.pk_gemm_reduce(64, 64, 64, FAKE, 64, FAKE, 64, d, 2, 32, 64, 0, FAKE, 32, None) == 1
+
+
+@needs_no_gpu
+def test_grouped_validation(lib):
+    ws = lib.pk_grouped_gemm_workspace_size(4096, 8, 32)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.pk_grouped_gemm_workspace_size(4096, 0, 32) == 0
+    assert lib.pk_grouped_gemm_workspace_size(4096, 8, 2000) == 0
+    args = lambda **kw: [kw.get("T", 16), kw.get("top_k", 2), FAKE, kw.get("E", 8),
+                         kw.get("begin", 0), kw.get("nl", 4), FAKE, kw.get("ldx", 64),
+                         kw.get("K", 64), FAKE, kw.get("N", 64), FAKE, FAKE, FAKE,
+                         kw.get("ldy", 64), kw.get("dt", 0), FAKE, kw.get("ws", 1 << 20), None]
+    assert lib.pk_grouped_gemm(*args(top_k=0)) == 1
+    assert lib.pk_grouped_gemm(*args(nl=0)) == 1
+    assert lib.pk_grouped_gemm(*args(begin=6)) == 1          # local range beyond num_experts
+    assert lib.pk_grouped_gemm(*args(ws=16)) == 1            # workspace too small
+    assert lib.pk_grouped_gemm(*args(K=60, ldx=64)) == 2
+    assert lib.pk_grouped_gemm(*args(dt=9)) == 1
+    assert lib.pk_grouped_gemm(*args(ldx=32)) == 1
+
+
+def test_python_binding_refuses_host_tensors(lib):
+    import torch
+    import gemm_tile_granular_bf16_amd as pk
+    a = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        pk.gemm(a, torch.zeros(8, 8, dtype=torch.bfloat16), torch.zeros(4, 8))

@@ -1,0 +1,141 @@
+"""pk_gemm (AG+GEMM local share) against the oracle on the GPU, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import pk_inputs
+from _gpu import dev_bf16, host_bits, host_f32, log, require_gpu, sample_rows
+from _parity import bf16_bits_to_f64, check_bf16, check_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pk():
+    return require_gpu()
+
+
+def _run(pk, A_bits, B_bits, chunks=1, first_chunk=0, dtype=torch.float32):
+    M, K = A_bits.shape
+    N = B_bits.shape[1]
+    A = dev_bf16(A_bits)
+    rows = (M + chunks - 1) // chunks
+    parts = [A[i * rows:min(M, (i + 1) * rows)] for i in range(chunks)]
+    # separate allocations per chunk, like gathered buffers from different ranks
+    parts = [p.clone() for p in parts]
+    B = dev_bf16(B_bits)
+    C = torch.full((M, N), float("nan"), dtype=dtype, device="cuda")
+    pk.gemm(parts, B, C, first_chunk=first_chunk)
+    torch.cuda.synchronize()
+    return C
+
+
+SHAPES = [  # (M, N, K, chunks, first_chunk): tails in every dimension, every tile shape
+    (1, 8, 8, 1, 0),
+    (17, 24, 40, 1, 0),
+    (300, 136, 200, 2, 1),
+    (513, 264, 1032, 3, 2),
+    (256, 256, 64, 1, 0),
+    (700, 520, 96, 5, 4),
+    (4100, 2056, 72, 4, 1),    # 256x128 tiles
+    (8200, 4104, 72, 2, 1),    # 256x256 tiles, ragged in M and N, K tail
+]
+
+
+@pytest.mark.parametrize("M,N,K,chunks,first", SHAPES, ids=[str(s) for s in SHAPES])
+def test_parity_small(pk, oracle_mod, M, N, K, chunks, first):
+    log("pk_gemm parity M=%d N=%d K=%d chunks=%d first=%d" % (M, N, K, chunks, first))
+    A = pk_inputs.normal_bf16((M, K), 1.0, 10 + M)
+    B = pk_inputs.normal_bf16((K, N), 1.0, 20 + N)
+    o = oracle_mod.default()
+    R = o.gemm(A, B)
+    absR = np.abs(bf16_bits_to_f64(A)) @ np.abs(bf16_bits_to_f64(B))
+    C32 = host_f32(_run(pk, A, B, chunks, first, torch.float32))
+    check_f32(C32, R, absR, K, "f32")
+    C16 = host_bits(_run(pk, A, B, chunks, first, torch.bfloat16))
+    check_bf16(C16, R, o.round_bf16(R), absR, K, "bf16")
+
+
+def test_all_ones_gives_K(pk):
+    M, N, K = 300, 264, 1024
+    one = pk_inputs.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    A = np.full((M, K), one, np.uint16)
+    B = np.full((K, N), one, np.uint16)
+    assert np.all(host_f32(_run(pk, A, B)) == 1024.0)
+    assert np.all(host_bits(_run(pk, A, B, dtype=torch.bfloat16)) == 0x4480)
+
+
+def test_identity_reproduces_B(pk):
+    K, N = 512, 200
+    I = pk_inputs.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    B = pk_inputs.normal_bf16((K, N), 1.0, 5)
+    assert np.array_equal(host_bits(_run(pk, I, B, chunks=3, first_chunk=2, dtype=torch.bfloat16)), B)
+    assert np.array_equal(host_f32(_run(pk, I, B)), bf16_bits_to_f64(B).astype(np.float32))
+
+
+def test_rank_one_outer_product(pk, oracle_mod):
+    M, N, K = 333, 136, 64
+    u = pk_inputs.normal_bf16((M,), 1.0, 3)
+    v = pk_inputs.normal_bf16((N,), 1.0, 4)
+    A = np.zeros((M, K), np.uint16); A[:, 5] = u
+    B = np.zeros((K, N), np.uint16); B[5, :] = v
+    exact = np.outer(bf16_bits_to_f64(u), bf16_bits_to_f64(v))  # exact in fp32 (8x8 bits)
+    assert np.array_equal(host_f32(_run(pk, A, B)), exact.astype(np.float32))
+    assert np.array_equal(host_bits(_run(pk, A, B, dtype=torch.bfloat16)),
+                          oracle_mod.round_bf16(exact))
+
+
+def test_small_integers_bit_exact(pk, oracle_mod):
+    M, N, K = 520, 392, 1024
+    A = pk_inputs.small_int_bf16((M, K), -4, 4, 61)
+    B = pk_inputs.small_int_bf16((K, N), -4, 4, 62)
+    R = oracle_mod.gemm(A, B)
+    assert np.array_equal(host_f32(_run(pk, A, B, chunks=2)).astype(np.float64), R)
+
+
+def test_first_chunk_does_not_change_result(pk):
+    M, N, K = 1024, 264, 128
+    A = pk_inputs.normal_bf16((M, K), 1.0, 71)
+    B = pk_inputs.normal_bf16((K, N), 1.0, 72)
+    ref = host_f32(_run(pk, A, B, chunks=4, first_chunk=0))
+    for f in (1, 3):
+        assert np.array_equal(host_f32(_run(pk, A, B, chunks=4, first_chunk=f)), ref)
+
+
+def test_k_zero_stores_zeros_and_empty_is_noop(pk):
+    Ad = torch.zeros((40, 0), dtype=torch.bfloat16, device="cuda")
+    Bd = torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")
+    Cd = torch.full((40, 16), 7.0, device="cuda")
+    pk.gemm(Ad, Bd, Cd)
+    torch.cuda.synchronize()
+    assert torch.all(Cd == 0)
+    Ce = torch.full((0, 16), 7.0, device="cuda")
+    pk.gemm(torch.zeros((0, 8), dtype=torch.bfloat16, device="cuda"),
+            torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda"), Ce)
+
+
+def test_sixteen_chunks_ragged_last(pk, oracle_mod):
+    M, N, K = 16 * 40 - 13, 72, 48
+    A = pk_inputs.normal_bf16((M, K), 1.0, 81)
+    B = pk_inputs.normal_bf16((K, N), 1.0, 82)
+    R = oracle_mod.gemm(A, B)
+    absR = np.abs(bf16_bits_to_f64(A)) @ np.abs(bf16_bits_to_f64(B))
+    check_f32(host_f32(_run(pk, A, B, chunks=16, first_chunk=9)), R, absR, K, "16 chunks")
+
+
+def test_ag_local_share_8192_sampled(pk, oracle_mod):
+    """The AG+GEMM local share at N=8192: A 8 row-chunks of 1024 x 8192, B 8192 x 1024, bf16 C --
+    the launch the benchmark times; checked on sampled rows against the oracle."""
+    w = pk_inputs.WORKLOADS["ag_8192"]
+    log("AG 8192: generating inputs")
+    A = pk_inputs.normal_bf16((w.M, w.K), w.std_a, w.seed_a)
+    B = pk_inputs.normal_bf16((w.K, w.N), w.std_b, w.seed_b)
+    log("AG 8192: running")
+    C16 = host_bits(_run(pk, A, B, chunks=w.chunks, dtype=torch.bfloat16))
+    C32 = host_f32(_run(pk, A, B, chunks=w.chunks, dtype=torch.float32))
+    rows = sample_rows(w.M, 40, 91, must=[0, 1023, 1024, 4095, 4096, 8191])
+    o = oracle_mod.default()
+    R = o.gemm_rows(A, B, rows)
+    absR = np.abs(bf16_bits_to_f64(A[rows])) @ np.abs(bf16_bits_to_f64(B))
+    check_f32(C32[rows], R, absR, w.K, "AG f32")
+    check_bf16(C16[rows], R, o.round_bf16(R), absR, w.K, "AG bf16")

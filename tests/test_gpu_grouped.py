@@ -1,0 +1,146 @@
+"""pk_grouped_gemm (token dispatch + expert GEMM) against the oracle on the GPU, through the C
+ABI: dispatch bit-exact, the grouped product within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import pk_inputs
+from _gpu import dev_bf16, host_bits, host_f32, log, require_gpu
+from _parity import bf16_bits_to_f64, check_bf16, check_f32
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -7
+
+
+@pytest.fixture(scope="module")
+def pk():
+    return require_gpu()
+
+
+def _run(pk, ids, X_bits, W_bits, num_experts, begin, dtype=torch.float32):
+    T, top_k = ids.shape
+    nl, K, N = W_bits.shape
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    X = dev_bf16(X_bits) if X_bits.size else torch.zeros((T, K), dtype=torch.bfloat16, device="cuda")
+    W = dev_bf16(W_bits)
+    offsets = torch.full((nl + 1,), SENTINEL, dtype=torch.int32, device="cuda")
+    perm = torch.full((max(T * top_k, 1),), SENTINEL, dtype=torch.int32, device="cuda")
+    Y = torch.full((max(T * top_k, 1), N), float("nan"), dtype=dtype, device="cuda")
+    ws = torch.empty(pk.grouped_gemm_workspace_size(T, top_k, nl), dtype=torch.uint8, device="cuda")
+    pk.grouped_gemm(ids_d, X, W, num_experts, begin, offsets, perm, Y, ws)
+    torch.cuda.synchronize()
+    return offsets.cpu().numpy(), perm.cpu().numpy(), Y
+
+
+def _check_dispatch(o, ids, E, begin, nl, off, perm):
+    c, woff, wperm = o.dispatch(ids, E, begin, nl)
+    assert np.array_equal(off, woff), "offsets"
+    rows = int(woff[-1])
+    assert np.array_equal(perm[:rows], wperm), "perm"
+    assert np.all(perm[rows:] == SENTINEL), "perm past the local rows must be untouched"
+    return woff, wperm
+
+
+ROUTINGS = [  # (T, top_k, E, begin, nl, zipf s, seed)
+    (4096, 8, 256, 0, 32, 1.1, 6003),   # the MoE workload's routing
+    (1000, 4, 64, 16, 16, 0.8, 11),
+    (777, 6, 300, 290, 10, 1.3, 12),
+    (1, 8, 16, 0, 16, 1.1, 13),         # a single token
+    (5000, 2, 1024, 0, 1024, 1.0, 14),  # many local experts, many slices
+]
+
+
+@pytest.mark.parametrize("T,top_k,E,begin,nl,s,seed", ROUTINGS, ids=[str(r[:5]) for r in ROUTINGS])
+def test_dispatch_bit_exact(pk, oracle_mod, T, top_k, E, begin, nl, s, seed):
+    log("dispatch T=%d top_k=%d E=%d local [%d,%d)" % (T, top_k, E, begin, begin + nl))
+    ids = pk_inputs.zipf_topk(T, E, top_k, s, seed)
+    W = np.zeros((nl, 8, 8), np.uint16)
+    X = np.zeros((T, 8), np.uint16)
+    off, perm, _ = _run(pk, ids, X, W, E, begin)
+    _check_dispatch(oracle_mod.default(), ids, E, begin, nl, off, perm)
+
+
+def test_dispatch_special_cases(pk, oracle_mod):
+    o = oracle_mod.default()
+    cases = [
+        (np.full((10, 2), 7, np.int32), 8, 0, 4),                        # nothing local
+        (np.full((9, 1), 2, np.int32), 4, 0, 4),                         # all to one expert
+        (np.array([[4, 5], [2, -1], [3, 2], [2, 1000]], np.int32), 4, 2, 2),  # invalid ids
+    ]
+    for ids, E, begin, nl in cases:
+        off, perm, _ = _run(pk, ids, np.zeros((ids.shape[0], 8), np.uint16),
+                            np.zeros((nl, 8, 8), np.uint16), E, begin)
+        _check_dispatch(o, ids, E, begin, nl, off, perm)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_grouped_parity_small(pk, oracle_mod, dtype):
+    T, top_k, E, begin, nl, K, N = 300, 4, 16, 3, 6, 136, 264
+    ids = pk_inputs.zipf_topk(T, E, top_k, 0.9, 21)
+    X = pk_inputs.normal_bf16((T, K), 1.0, 22)
+    W = pk_inputs.normal_bf16((nl, K, N), 0.5, 23)
+    off, perm, Y = _run(pk, ids, X, W, E, begin, dtype)
+    o = oracle_mod.default()
+    woff, wperm = _check_dispatch(o, ids, E, begin, nl, off, perm)
+    R = o.grouped_gemm(woff, wperm, top_k, X, W)
+    rows = int(woff[-1])
+    absR = np.zeros_like(R)
+    x, w = np.abs(bf16_bits_to_f64(X)), np.abs(bf16_bits_to_f64(W))
+    for e in range(nl):
+        seg = slice(woff[e], woff[e + 1])
+        absR[seg] = x[wperm[seg] // top_k] @ w[e]
+    if dtype == torch.float32:
+        got = host_f32(Y[:rows])
+        check_f32(got, R, absR, K, "grouped f32")
+        assert np.all(np.isnan(host_f32(Y[rows:]))), "rows past the local rows must be untouched"
+    else:
+        check_bf16(host_bits(Y[:rows]), R, o.round_bf16(R), absR, K, "grouped bf16")
+
+
+def test_selection_weights_exact(pk, oracle_mod):
+    """W_e[k, n] = 2^(e mod 8 - 4) if k == n + c_e else 0 and X[t, k] = (t+1) 2^(k mod 8 - 4):
+    Y[j, n] = 2^(e mod 8 - 4) X[perm[j] // top_k, n + c_e] exactly, pinning gather, offsets and
+    the expert choice through the GPU product."""
+    T, top_k, E, nl, K, N = 200, 3, 12, 6, 64, 16
+    ids = pk_inputs.zipf_topk(T, E, top_k, 0.5, 91)
+    Xv = (np.arange(T)[:, None] + 1.0) * 2.0 ** (np.arange(K)[None, :] % 8 - 4)
+    shift = [(3 * e) % (K - N + 1) for e in range(nl)]
+    Wv = np.zeros((nl, K, N))
+    for e in range(nl):
+        Wv[e, np.arange(N) + shift[e], np.arange(N)] = 2.0 ** (e % 8 - 4)
+    X = pk_inputs.f32_to_bf16_bits(Xv.astype(np.float32))
+    W = pk_inputs.f32_to_bf16_bits(Wv.astype(np.float32))
+    off, perm, Y = _run(pk, ids, X, W, E, 0)
+    got = host_f32(Y)
+    for e in range(nl):
+        for j in range(off[e], off[e + 1]):
+            t = perm[j] // top_k
+            assert np.array_equal(got[j], (2.0 ** (e % 8 - 4) * Xv[t, shift[e]:shift[e] + N]).astype(np.float32))
+
+
+def test_moe_workload_sampled(pk, oracle_mod):
+    """The MoE workload: 4096 tokens, D=7168, top_k=8 over 256 experts with 32 local, Zipf(1.1)
+    routing; grouped GEMM 7168 -> 2048 per expert, bf16 output.  Dispatch bit-exact; sampled rows
+    (first and last row of every expert plus random rows) against the oracle."""
+    w = pk_inputs.WORKLOADS["moe_dispatch"]
+    log("MoE: generating inputs")
+    ids, X, W = pk_inputs.moe_inputs(w)
+    log("MoE: running")
+    off, perm, Y = _run(pk, ids, X, W, w.num_experts, w.expert_begin, torch.bfloat16)
+    o = oracle_mod.default()
+    woff, wperm = _check_dispatch(o, ids, w.num_experts, w.expert_begin, w.num_local, off, perm)
+    rng = np.random.Generator(np.random.PCG64(5))
+    rows = set()
+    for e in range(w.num_local):
+        if woff[e + 1] > woff[e]:
+            rows.update([int(woff[e]), int(woff[e + 1]) - 1])
+    rows.update(int(r) for r in rng.integers(0, woff[-1], size=16))
+    rows = sorted(rows)
+    Yh = host_bits(Y)
+    expert_of = np.searchsorted(woff, np.array(rows), side="right") - 1
+    for j, e in zip(rows, expert_of):
+        xrow = np.ascontiguousarray(X[wperm[j] // w.top_k][None, :])
+        R = o.gemm(xrow, W[e])
+        absR = np.abs(bf16_bits_to_f64(xrow)) @ np.abs(bf16_bits_to_f64(W[e]))
+        check_bf16(Yh[j][None, :], R, o.round_bf16(R), absR, w.K, "MoE row %d" % j)

@@ -1,0 +1,170 @@
+"""pk_gemm_reduce (GEMM+RS / GEMM+AR receiving side, optional bf16 cast) against the oracle on the
+GPU, through the C ABI, in both reduction modes."""
+import numpy as np
+import pytest
+import torch
+
+import pk_inputs
+from _gpu import dev_bf16, host_bits, host_f32, log, require_gpu, sample_rows
+from _parity import bf16_bits_to_f64, check_f32, gamma
+
+pytestmark = pytest.mark.gpu
+
+MODES = [0, 1]  # PK_REDUCE_ATOMIC, PK_REDUCE_OWNER
+MODE_IDS = ["atomic", "owner"]
+
+
+@pytest.fixture(scope="module")
+def pk():
+    return require_gpu()
+
+
+def _absbound(prods):
+    return sum(np.abs(bf16_bits_to_f64(a)) @ np.abs(bf16_bits_to_f64(b)) for a, b in prods)
+
+
+def _check_reduce(got, R, prods, D0, what):
+    K_total = sum(a.shape[1] for a, _ in prods)
+    absR = _absbound(prods) + (np.abs(D0.astype(np.float64)) if D0 is not None else 0.0)
+    check_f32(got, R, absR, K_total + len(prods) + 1, what)
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_tiny_eight_producers(pk, oracle_mod, mode):
+    """8 producers (A_r 512x64, B_r 64x512 ~N(0,1)) into one zero 512x512 fp32 destination.  In
+    atomic mode they run on 8 concurrent streams, so their adds really interleave."""
+    w = pk_inputs.WORKLOADS["rs_tiny"]
+    prods = [pk_inputs.producer_operands(w, p) for p in range(w.producers)]
+    D = torch.zeros((w.M, w.N), device="cuda")
+    dev = [(dev_bf16(a), dev_bf16(b)) for a, b in prods]
+    torch.cuda.synchronize()
+    if mode == 0:
+        streams = [torch.cuda.Stream() for _ in dev]
+        for s, (a, b) in zip(streams, dev):
+            pk.gemm_reduce(a, b, D, mode=mode, stream=s)
+    else:
+        for a, b in dev:
+            pk.gemm_reduce(a, b, D, mode=mode)
+    torch.cuda.synchronize()
+    R = oracle_mod.reduce(None, prods)
+    _check_reduce(host_f32(D), R, prods, None, "tiny")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_integer_producers_bit_exact(pk, oracle_mod, mode):
+    M, N, K = 512, 512, 64
+    prods = [(pk_inputs.small_int_bf16((M, K), -3, 3, 300 + p),
+              pk_inputs.small_int_bf16((K, N), -3, 3, 400 + p)) for p in range(8)]
+    D0 = np.random.Generator(np.random.PCG64(9)).integers(-100, 100, size=(M, N)).astype(np.float32)
+    D = torch.from_numpy(D0).cuda()
+    streams = [torch.cuda.Stream() for _ in prods] if mode == 0 else [None] * len(prods)
+    torch.cuda.synchronize()
+    for s, (a, b) in zip(streams, prods):
+        pk.gemm_reduce(dev_bf16(a), dev_bf16(b), D, mode=mode, stream=s)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(D).astype(np.float64), oracle_mod.reduce(D0, prods))
+
+
+def test_all_ones_eight_producers_give_512(pk):
+    one = pk_inputs.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    a = dev_bf16(np.full((512, 64), one, np.uint16))
+    b = dev_bf16(np.full((64, 512), one, np.uint16))
+    D = torch.zeros((512, 512), device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(8)]
+    torch.cuda.synchronize()
+    for s in streams:
+        pk.gemm_reduce(a, b, D, mode=0, stream=s)
+    torch.cuda.synchronize()
+    assert torch.all(D == 512.0)
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_shard_map_coordinate_encoding(pk, mode):
+    """K = 8 with A[i,0] = i // 256, A[i,1] = i % 256, B[0,:] = 256, B[1,:] = 1 gives C[i,j] = i
+    exactly (and the transposed encoding gives j): every element of 8 separately allocated shards
+    must hold its own global row (column) index, pinning the tile-to-shard map bit-exactly."""
+    M, N, K, S = 2048, 1024, 8, 8
+    i = np.arange(M)
+    j = np.arange(N)
+    Ar = np.zeros((M, K), np.float32); Ar[:, 0] = i // 256; Ar[:, 1] = i % 256
+    Br = np.zeros((K, N), np.float32); Br[0, :] = 256; Br[1, :] = 1
+    Ac = np.zeros((M, K), np.float32); Ac[:, 0] = 1; Ac[:, 1] = 1
+    Bc = np.zeros((K, N), np.float32); Bc[0, :] = (j // 256) * 256; Bc[1, :] = j % 256
+    for Af, Bf, want in ((Ar, Br, np.repeat(i[:, None], N, 1)), (Ac, Bc, np.repeat(j[None, :], M, 0))):
+        shards = [torch.zeros((M // S, N), device="cuda") for _ in range(S)]
+        pk.gemm_reduce(dev_bf16(pk_inputs.f32_to_bf16_bits(Af)), dev_bf16(pk_inputs.f32_to_bf16_bits(Bf)),
+                       shards, mode=mode)
+        torch.cuda.synchronize()
+        got = np.concatenate([host_f32(s) for s in shards], axis=0)
+        assert np.array_equal(got, want.astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_ragged_shards_and_padded_destination(pk, oracle_mod, mode):
+    M, N, K = 1000, 136, 200  # 4 shards of 256 rows (last 232), K tail, padded leading dim
+    A = pk_inputs.normal_bf16((M, K), 1.0, 111)
+    B = pk_inputs.normal_bf16((K, N), 1.0, 112)
+    D0 = np.random.Generator(np.random.PCG64(113)).standard_normal((M, N)).astype(np.float32)
+    base = torch.zeros((M, 160), device="cuda")
+    base[:, :N] = torch.from_numpy(D0).cuda()
+    base[:, N:] = 5.0
+    shards = [base[r:r + 256, :N] for r in range(0, M, 256)]
+    pk.gemm_reduce(dev_bf16(A), dev_bf16(B), shards, mode=mode)
+    torch.cuda.synchronize()
+    got = host_f32(base)
+    assert np.all(got[:, N:] == 5.0)  # padding untouched
+    R = oracle_mod.reduce(D0, [(A, B)])
+    _check_reduce(got[:, :N], R, [(A, B)], D0, "ragged")
+
+
+def test_k_zero_adds_nothing_and_cast_still_runs(pk, oracle_mod):
+    M, N = 96, 64
+    D0 = np.random.Generator(np.random.PCG64(7)).standard_normal((M, N)).astype(np.float32)
+    D = torch.from_numpy(D0).cuda()
+    out = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    pk.gemm_reduce(torch.zeros((M, 0), dtype=torch.bfloat16, device="cuda"),
+                   torch.zeros((0, N), dtype=torch.bfloat16, device="cuda"), D, out_bf16=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(D), D0)
+    assert np.array_equal(host_bits(out), oracle_mod.cast_f32_bf16(D0))
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_rs_local_share_8192_sampled(pk, oracle_mod, mode):
+    """GEMM+RS local share at N=8192: A 8192x1024 times B 1024x8192 added into an 8192x8192 fp32
+    destination pre-filled with 7 other producers' partials, viewed as 8 shards of 1024 rows --
+    the launch the benchmark times; sampled rows against the oracle."""
+    w = pk_inputs.WORKLOADS["rs_8192"]
+    log("RS 8192 mode=%d: generating inputs" % mode)
+    A, B = pk_inputs.producer_operands(w, 0)
+    D0 = pk_inputs.rs_prefill(w.M, w.N, w.prefill_partials, w.prefill_std, w.prefill_seed)
+    D = torch.from_numpy(D0).cuda()
+    shards = list(D.split(w.M // w.shards))
+    log("RS 8192: running")
+    pk.gemm_reduce(dev_bf16(A), dev_bf16(B), shards, mode=mode)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.M, 40, 121, must=[0, 1023, 1024, 5000, 8191])
+    got = host_f32(D[rows])
+    R = oracle_mod.reduce(D0[rows], [(np.ascontiguousarray(A[rows]), B)])
+    _check_reduce(got, R, [(A[rows], B)], D0[rows], "RS 8192")
+
+
+def test_ar_local_share_16384_with_cast(pk, oracle_mod):
+    """GEMM+AR local share at N=16384: A 16384x2048 times B 2048x16384 reduced into a full
+    16384x16384 fp32 destination (one shard, starts at zero), then the bf16 cast pass.  The
+    reduction is checked on sampled rows; the cast bit-exactly on every element against the
+    oracle's rounding of the GPU's own fp32 destination."""
+    w = pk_inputs.WORKLOADS["ar_16384"]
+    log("AR 16384: generating inputs")
+    A, B = pk_inputs.producer_operands(w, 0)
+    D = torch.zeros((w.M, w.N), device="cuda")
+    out = torch.zeros((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    log("AR 16384: running")
+    pk.gemm_reduce(dev_bf16(A), dev_bf16(B), D, mode=1, out_bf16=out)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.M, 24, 131, must=[0, 16383, 8192])
+    R = oracle_mod.reduce(None, [(np.ascontiguousarray(A[rows]), B)])
+    _check_reduce(host_f32(D[rows]), R, [(A[rows], B)], None, "AR 16384")
+    log("AR 16384: cast check")
+    Dh = host_f32(D)
+    assert np.array_equal(host_bits(out), oracle_mod.cast_f32_bf16(Dh))
