@@ -41,12 +41,8 @@ pk::TileCfgId pick_store_cfg(int64_t M, int64_t N) {
     return pk::CFG_128x128;
 }
 
-// Tile shape for the reduction epilogues: two resident workgroups per CU so that one workgroup's
-// destination traffic overlaps the other's MFMAs.
-pk::TileCfgId pick_reduce_cfg(int64_t M, int64_t N) {
-    if (ceil_div(M, 256) * ceil_div(N, 128) >= 256) return pk::CFG_256x128_2WG;
-    return pk::CFG_128x128;
-}
+// Tile shape for the reduction epilogues: the same rule as the stores.
+pk::TileCfgId pick_reduce_cfg(int64_t M, int64_t N) { return pick_store_cfg(M, N); }
 
 }  // namespace
 

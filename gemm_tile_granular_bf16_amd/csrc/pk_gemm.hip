@@ -8,60 +8,70 @@
 // (tiles staged through swizzled on-chip memory, multi-stage buffering, L2-aware block order),
 // re-derived for CDNA4:
 //
-//  * MFMA v_mfma_f32_32x32x16_bf16: every wave owns a (FM*32) x (FN*32) accumulator block held in
-//    registers; operands come from LDS as 16-byte reads (8 consecutive k per lane).
-//  * Operand staging: A (M x K, k-contiguous) is copied HBM -> registers -> LDS unchanged.  B
-//    (K x N row-major, n-contiguous) is loaded as 8x8 sub-blocks and transposed in registers so
-//    that LDS holds B^T (n rows, k-contiguous), the layout the MFMA B operand wants.
-//  * LDS rows of BK bf16 are split in 16-byte chunks whose position is XOR-swizzled with the row
-//    index (the article's bank = column XOR (row >> shift) scheme, widened so that 8 or 16
-//    consecutive rows of a 16-byte read land on distinct banks).
-//  * Two LDS stages: global loads of k-step t+1 are in flight while the MFMAs of step t run; one
-//    workgroup barrier per k-step.
-//  * Grid: workgroups are dealt round-robin to the 8 XCDs; block ids are remapped so that each XCD
-//    works on one contiguous run of logical tiles, and logical tiles are rastered in groups of
-//    tile rows, so operand panels are reused from that XCD's L2.
+//  * MFMA v_mfma_f32_32x32x16_bf16: every wave owns an (FM*32) x (FN*32) accumulator block held
+//    in registers.
+//  * Operand staging without registers: both operands go HBM -> LDS with global_load_lds_dwordx4
+//    (each lane moves 16 bytes into its slot of a 1 KB wave-contiguous LDS block), so a whole
+//    stage is in flight while the previous one feeds the MFMAs.  A (M x K, k-contiguous) is
+//    stored as rows of BK bf16; B (K x N, n-contiguous) is stored as it is in memory, rows of BN
+//    bf16, and read with ds_read_b64_tr_b16, whose 16-lane transpose hands each lane the 4
+//    consecutive k of one column that the MFMA B operand wants (two reads give the 8 k of one
+//    32x32x16 operand).
+//  * LDS rows are split in 16-byte chunks whose position is XOR-swizzled with the row (the
+//    article's bank = column XOR (row >> shift) scheme): for A the chunk index is XORed with
+//    row ^ (row >> 3), for B with 10 * (k mod 4); both make the MFMA operand reads free of bank
+//    conflicts.  Since a DMA lane's LDS slot is fixed, the swizzle is applied when choosing
+//    which global chunk each lane fetches.
+//  * ST LDS stages, one workgroup barrier per k-step, loads for step t+ST-1 issued right after
+//    it; explicit s_waitcnt vmcnt instead of __syncthreads (whose fence would drain every load
+//    in flight).  The MFMAs of the last k16 slice of a step are issued after the barrier, so they
+//    overlap the first LDS reads of the next step.  A ragged last k-step is staged through
+//    registers with zero fill.
+//  * Grid: workgroups are dealt round-robin to the 8 XCDs; block ids are remapped so that each
+//    XCD works on one contiguous run of logical tiles, and logical tiles are rastered in groups
+//    of tile rows, so operand panels are reused from that XCD's L2.
 #include "pk_internal.h"
 
 namespace pk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#define PK_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MIN_WG_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int ST_>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, ST = ST_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int CPR = BK / 8;  // 16-byte chunks per LDS row
-    static constexpr int A_LOADS = BM * CPR / NT;
-    static constexpr int B_SUBS = (BK / 8) * (BN / 8);  // 8 (k) x 8 (n) sub-blocks
-    static constexpr int B_LOADS = (B_SUBS + NT - 1) / NT;
-    static constexpr int ROW_BYTES = BK * 2;
-    static constexpr int LDS_A = BM * ROW_BYTES;
-    static constexpr int LDS_B = BN * ROW_BYTES;
-    static constexpr int LDS_STAGE = LDS_A + LDS_B;
-    static constexpr int LDS_BYTES = 2 * LDS_STAGE;
-    static constexpr int MIN_WG = MIN_WG_;
-    static_assert((BM * CPR) % NT == 0, "A chunks must split evenly over threads");
-    static_assert(NT % CPR == 0, "each thread keeps one k-chunk of A");
-    static_assert(BK == 32 || BK == 64, "LDS swizzle defined for 64- and 128-byte rows");
+    static constexpr int KK = BK / 16;                   // MFMA k16 slices per step
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES, LDS_BYTES = ST * STAGE;
+    static constexpr int AI = A_BYTES / 1024 / NW;       // 1 KB DMA blocks per wave per step
+    static constexpr int BI = B_BYTES / 1024 / NW;
+    static constexpr int LPS = AI + BI;                  // DMA instructions per wave per step
+    static constexpr int CPRA = BK / 8, CPRB = BN / 8;   // 16-byte chunks per LDS row
+    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA blocks");
+    static_assert(BK == 64, "A swizzle defined for 128-byte rows");
+    static_assert(CPRB >= 16, "B swizzle needs at least 16 chunks per row");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 MFMA blocks");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KB per CU");
+    static_assert(ST >= 2 && ST <= 3, "pipeline depth");
 };
 
-using Cfg256x256 = Cfg<256, 256, 64, 2, 2, 1>;
-using Cfg256x128 = Cfg<256, 128, 64, 2, 2, 1>;
-using Cfg256x128x2 = Cfg<256, 128, 32, 2, 2, 2>;
-using Cfg128x128 = Cfg<128, 128, 64, 2, 2, 1>;
+using Cfg256x256 = Cfg<256, 256, 64, 2, 4, 2>;  // 8 waves of 128x64, 128 KB LDS
+using Cfg256x128 = Cfg<256, 128, 64, 2, 2, 3>;  // 4 waves of 128x64, 144 KB LDS
+using Cfg128x128 = Cfg<128, 128, 64, 2, 2, 2>;  // 4 waves of 64x64, 64 KB LDS
 
 TileShape tile_shape(TileCfgId cfg) {
     switch (cfg) {
         case CFG_256x256: return {256, 256};
         case CFG_256x128: return {256, 128};
-        case CFG_256x128_2WG: return {256, 128};
         default: return {128, 128};
     }
 }
@@ -70,16 +80,23 @@ TileShape tile_shape(TileCfgId cfg) {
 // Small device helpers
 // ------------------------------------------------------------------------------------------------
 
-// 16-byte chunk position inside an LDS row, XOR-swizzled with the row.
-template <int CPR>
-__device__ __forceinline__ int lds_offset(int row, int chunk) {
-    int s;
-    if constexpr (CPR == 8)
-        s = (row ^ (row >> 3)) & 7;
-    else
-        s = ((row >> 1) ^ (row >> 3)) & 3;
-    return row * (CPR * 16) + ((chunk ^ s) << 4);
+__device__ __forceinline__ int swz_a(int row) { return (row ^ (row >> 3)) & 7; }
+template <int CPRB>
+__device__ __forceinline__ int swz_b(int k) { return (10 * (k & 3)) & (CPRB - 1); }
+
+// 16 bytes per lane HBM -> LDS; lane i lands at lds_base + 16*i (lds_base is wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, char* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, PK_LDS_PTR(void, lds_base), 16, 0, 0);
 }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0]+[15:14], expcnt[6:4],
+// lgkmcnt[11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Round to nearest even, fp32 -> bf16 bits (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -115,14 +132,14 @@ __device__ __forceinline__ bool xcd_remap(int b, int total, int& L) {
 // ------------------------------------------------------------------------------------------------
 
 template <class C, bool GROUPED, int EPI>
-__global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm_tile_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+__global__ __launch_bounds__(C::NT, 1) void gemm_tile_kernel(GemmArgs p) {
+    __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wy = wave / C::WAVES_N;
-    const int wx = wave % C::WAVES_N;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wy = w / C::WAVES_N;
+    const int wx = w % C::WAVES_N;
 
     const int64_t M = p.M, N = p.N, K = p.K;
     const int tiles_n = (int)((N + C::BN - 1) / C::BN);
@@ -167,95 +184,95 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm_tile_kernel(GemmArgs p)
         col0 = (int64_t)tn * C::BN;
     }
 
-    // ---- per-thread operand sources (fixed for the whole k-loop) ----------------------------
-    const int a_kc = tid % C::CPR;  // this thread's 16-byte k-chunk of A
-    const uint16_t* a_src[C::A_LOADS];
+    // ---- per-lane DMA sources (fixed for the whole k-loop) ----------------------------------
+    // DMA block b = j*NW + w covers LDS bytes [b*1 KB, (b+1)*1 KB) of the stage's A (or B) part;
+    // lane i owns 16-byte position q = b*64 + i.
+    const uint16_t* a_src[C::AI];
+    int a_kc[C::AI];  // first k of this lane's chunk, relative to the step
 #pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-        const int rl = (i * C::NT + tid) / C::CPR;
+    for (int j = 0; j < C::AI; ++j) {
+        const int q = (j * C::NW + w) * 64 + lane;
+        const int rl = q / C::CPRA;
+        const int c = (q % C::CPRA) ^ swz_a(rl);
+        a_kc[j] = c * 8;
         int64_t r = row0 + rl;
         if (r >= row_end) r = row0;  // masked row: read a valid one, never stored
         const uint16_t* src;
         if constexpr (GROUPED) {
             const int64_t token = p.perm[r] / p.top_k;
             src = p.a_ptr[0] + token * p.lda;
+        } else if (p.num_chunks == 1) {
+            src = p.a_ptr[0] + r * p.lda;
         } else {
-            if (p.num_chunks == 1) {
-                src = p.a_ptr[0] + r * p.lda;
-            } else {
-                const int c = (int)(r / p.chunk_rows);
-                src = pick(p.a_ptr, c) + (r - (int64_t)c * p.chunk_rows) * p.lda;
-            }
+            const int ch = (int)(r / p.chunk_rows);
+            src = pick(p.a_ptr, ch) + (r - (int64_t)ch * p.chunk_rows) * p.lda;
         }
-        a_src[i] = src + a_kc * 8;
+        a_src[j] = src + a_kc[j];
     }
-    const uint16_t* b_src[C::B_LOADS];
-    int b_kg[C::B_LOADS], b_ng[C::B_LOADS];
-    bool b_on[C::B_LOADS];
+    const uint16_t* b_src[C::BI];
+    int b_kr[C::BI];  // k row of this lane's chunk, relative to the step
 #pragma unroll
-    for (int j = 0; j < C::B_LOADS; ++j) {
-        const int s = j * C::NT + tid;
-        b_on[j] = s < C::B_SUBS;
-        const int ss = b_on[j] ? s : 0;
-        b_kg[j] = ss / (C::BN / 8);
-        b_ng[j] = ss % (C::BN / 8);
-        int64_t col = col0 + b_ng[j] * 8;
+    for (int j = 0; j < C::BI; ++j) {
+        const int q = (j * C::NW + w) * 64 + lane;
+        const int kr = q / C::CPRB;
+        const int c = (q % C::CPRB) ^ swz_b<C::CPRB>(kr);
+        b_kr[j] = kr;
+        int64_t col = col0 + c * 8;
         if (col >= N) col = 0;  // masked columns: read valid memory, never stored
-        b_src[j] = Bm + (int64_t)(b_kg[j] * 8) * p.ldb + col;
+        b_src[j] = Bm + (int64_t)kr * p.ldb + col;
     }
 
-    u32x4 ra[C::A_LOADS];
-    u32x4 rb[C::B_LOADS][8];
-
-    auto load_step = [&](int64_t k0, bool tail) {
+    // Full k-step: every lane DMAs its chunks.
+    auto issue = [&](int64_t kt, int slot) {
+        char* sa = lds + slot * C::STAGE;
+        char* sb = sa + C::A_BYTES;
+        const int64_t k0 = kt * C::BK;
 #pragma unroll
-        for (int i = 0; i < C::A_LOADS; ++i) {
-            if (!tail || k0 + a_kc * 8 < K)
-                ra[i] = *(const u32x4*)(a_src[i] + k0);
-            else
-                ra[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < C::AI; ++j) dma16(a_src[j] + k0, sa + (j * C::NW + w) * 1024);
+#pragma unroll
+        for (int j = 0; j < C::BI; ++j) dma16(b_src[j] + k0 * p.ldb, sb + (j * C::NW + w) * 1024);
+    };
+    // Ragged last k-step: same LDS positions, through registers, zero beyond K.
+    auto issue_tail = [&](int64_t kt, int slot) {
+        char* sa = lds + slot * C::STAGE;
+        char* sb = sa + C::A_BYTES;
+        const int64_t k0 = kt * C::BK;
+#pragma unroll
+        for (int j = 0; j < C::AI; ++j) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (k0 + a_kc[j] < K) v = *(const u32x4*)(a_src[j] + k0);
+            *(u32x4*)(sa + (j * C::NW + w) * 1024 + lane * 16) = v;
         }
 #pragma unroll
-        for (int j = 0; j < C::B_LOADS; ++j) {
-            if (!b_on[j]) continue;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int64_t k = k0 + b_kg[j] * 8 + r;
-                if (!tail || k < K)
-                    rb[j][r] = *(const u32x4*)(b_src[j] + (k0 + r) * p.ldb);
-                else
-                    rb[j][r] = u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int j = 0; j < C::BI; ++j) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (k0 + b_kr[j] < K) v = *(const u32x4*)(b_src[j] + k0 * p.ldb);
+            *(u32x4*)(sb + (j * C::NW + w) * 1024 + lane * 16) = v;
         }
     };
 
-    auto store_step = [&](int stage) {
-        char* sA = lds + stage * C::LDS_STAGE;
-        char* sB = sA + C::LDS_A;
+    // ---- per-lane LDS read offsets ------------------------------------------------------------
+    // A operand of block fm, slice kk: row wy*WTM + fm*32 + lane%32, k chunk 2*kk + lane/32.
+    int a_off[C::FM][C::KK];
 #pragma unroll
-        for (int i = 0; i < C::A_LOADS; ++i) {
-            const int rl = (i * C::NT + tid) / C::CPR;
-            *(u32x4*)(sA + lds_offset<C::CPR>(rl, a_kc)) = ra[i];
-        }
+    for (int fm = 0; fm < C::FM; ++fm) {
+        const int r = wy * C::WTM + fm * 32 + (lane & 31);
 #pragma unroll
-        for (int j = 0; j < C::B_LOADS; ++j) {
-            if (!b_on[j]) continue;
-            // rb[j][k] holds B[k][n0..n0+7] as 4 words of two bf16 (n even low, n odd high);
-            // emit, for each n, the 8 consecutive k as one 16-byte chunk.
+        for (int kk = 0; kk < C::KK; ++kk)
+            a_off[fm][kk] = r * (C::BK * 2) + (((kk * 2 + (lane >> 5)) ^ swz_a(r)) << 4);
+    }
+    // B operand of block fn, slice kk (two transposing reads, k rows +0..3 and +4..7):
+    // in 16-lane group G, lane i reads row 8*(G/2) + i/4 (+4), columns n + 4*(i%4) .. +3 where
+    // n = wx*WTN + fn*32 + 16*(G%2); the transpose gives lane i column n + i.
+    const int i16 = lane & 15, G = lane >> 4;
+    const int kq = (G >> 1) * 8 + (i16 >> 2);
+    const int swb = swz_b<C::CPRB>(kq);  // k mod 4 is the same for the +4 and +16*kk rows
+    int b_off[C::FN];
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int d = n >> 1;
-                u32x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = rb[j][2 * e][d], hi = rb[j][2 * e + 1][d];
-                    o[e] = (n & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                   : ((lo & 0xffffu) | (hi << 16));
-                }
-                *(u32x4*)(sB + lds_offset<C::CPR>(b_ng[j] * 8 + n, b_kg[j])) = o;
-            }
-        }
-    };
+    for (int fn = 0; fn < C::FN; ++fn) {
+        const int n = wx * C::WTN + fn * 32 + (G & 1) * 16 + (i16 & 3) * 4;
+        b_off[fn] = kq * (C::BN * 2) + (((n >> 3) ^ swb) << 4) + (n & 7) * 2;
+    }
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -265,40 +282,68 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm_tile_kernel(GemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
-    auto compute_step = [&](int stage) {
-        const char* sA = lds + stage * C::LDS_STAGE;
-        const char* sB = sA + C::LDS_A;
+    auto read_frags = [&](int slot, int kk, bf16x8* af, bf16x8* bfr) {
+        const char* sa = lds + slot * C::STAGE;
+        const char* sb = sa + C::A_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < C::BK / 16; ++kk) {
-            const int ch = kk * 2 + (lane >> 5);
-            bf16x8 af[C::FM], bfr[C::FN];
+        for (int fm = 0; fm < C::FM; ++fm) af[fm] = *(const bf16x8*)(sa + a_off[fm][kk]);
 #pragma unroll
-            for (int fm = 0; fm < C::FM; ++fm)
-                af[fm] = *(const bf16x8*)(sA + lds_offset<C::CPR>(wy * C::WTM + fm * 32 + (lane & 31), ch));
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-                bfr[fn] = *(const bf16x8*)(sB + lds_offset<C::CPR>(wx * C::WTN + fn * 32 + (lane & 31), ch));
-#pragma unroll
-            for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < C::FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+        for (int fn = 0; fn < C::FN; ++fn) {
+            const char* q = sb + b_off[fn] + kk * 16 * (C::BN * 2);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PK_LDS_PTR(i16x4, q));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PK_LDS_PTR(i16x4, q + 4 * (C::BN * 2)));
+            bfr[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
+    auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+    };
 
-    // ---- k-loop: loads of step t+1 in flight during the MFMAs of step t ---------------------
+    // ---- k-loop ---------------------------------------------------------------------------------
     const int64_t nk = (K + C::BK - 1) / C::BK;
+    const bool ragged = (K % C::BK) != 0;
+    auto stage_in = [&](int64_t kt, int slot) {
+        if (ragged && kt == nk - 1) issue_tail(kt, slot); else issue(kt, slot);
+    };
+    // vmcnt wait so that step `st` has landed, given DMAs issued for steps <= last
+    auto wait_step = [&](int64_t st, int64_t last) {
+        if constexpr (C::ST >= 3) {
+            if (last - st >= 1) { wait_vmcnt<C::LPS>(); return; }
+        }
+        wait_vmcnt<0>();
+    };
     if (nk > 0) {
-        load_step(0, C::BK > K);
-        store_step(0);
-        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < C::ST - 1; ++s)
+            if (s < nk) stage_in(s, s);
+        int64_t last = nk - 1 < C::ST - 2 ? nk - 1 : C::ST - 2;
+        wait_lgkmcnt0();
+        wait_step(0, last);
+        __builtin_amdgcn_s_barrier();
+        if (C::ST - 1 < nk) { stage_in(C::ST - 1, C::ST - 1); last = C::ST - 1; }
+        bf16x8 fa[2][C::FM], fb[2][C::FN];
+        read_frags(0, 0, fa[0], fb[0]);
         for (int64_t kt = 0; kt < nk; ++kt) {
-            const int stage = (int)(kt & 1);
-            const bool more = kt + 1 < nk;
-            if (more) load_step((kt + 1) * C::BK, (kt + 2) * C::BK > K);
-            compute_step(stage);
-            if (more) store_step(stage ^ 1);
-            __syncthreads();
+            const int slot = (int)(kt % C::ST);
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk) {
+                const int nb = (kk + 1) & 1;
+                if (kk + 1 < C::KK) {
+                    read_frags(slot, kk + 1, fa[nb], fb[nb]);
+                } else if (kt + 1 < nk) {
+                    // this wave's reads of step kt are complete, step kt+1 has landed everywhere
+                    wait_lgkmcnt0();
+                    wait_step(kt + 1, last);
+                    __builtin_amdgcn_s_barrier();
+                    if (kt + C::ST < nk) { stage_in(kt + C::ST, (int)((kt + C::ST) % C::ST)); last = kt + C::ST; }
+                    read_frags((int)((kt + 1) % C::ST), 0, fa[nb], fb[nb]);
+                }
+                mfmas(fa[kk & 1], fb[kk & 1]);
+            }
         }
     }
 
@@ -327,51 +372,95 @@ __global__ __launch_bounds__(C::NT, C::MIN_WG) void gemm_tile_kernel(GemmArgs p)
                     }
                 }
             }
+    } else if constexpr (EPI == EPI_OWNER_F32) {
+        // Owner-exclusive read-modify-write, staged through LDS (free after the k-loop): the
+        // tile is handled in WAVES_M bands of WTM rows.  The waves owning a band write their
+        // accumulators into LDS (fp32, row-major, 16-byte chunks XOR-swizzled so that rows 4
+        // apart use the other half of the banks); then every wave streams the band against the
+        // destination with 16-byte loads and stores, one destination row per wave instruction,
+        // all of a lane's loads in flight before the first add.
+        constexpr int ROWB = C::BN * 4;                 // bytes per LDS row
+        constexpr int CHUNKS = C::WTM * C::BN / 4;      // 16-byte chunks per band
+        constexpr int PER_T = CHUNKS / C::NT;           // chunks per thread per band
+        constexpr int CPRW = C::BN / 4;                 // chunks per row
+        static_assert(C::WTM * ROWB <= C::LDS_BYTES, "band must fit in LDS");
+        static_assert(CHUNKS % C::NT == 0 && C::NT % CPRW == 0, "whole rows per wave");
+        auto band_off = [&](int row, int chunk) {
+            return row * ROWB + ((chunk ^ (((row >> 2) & 1) << 3)) << 4);
+        };
+#pragma unroll
+        for (int band = 0; band < C::WAVES_M; ++band) {
+            wait_lgkmcnt0();
+            __builtin_amdgcn_s_barrier();
+            if (wy == band) {
+#pragma unroll
+                for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; ++fn) {
+                        const int col = wx * C::WTN + fn * 32 + lcol;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = fm * 32 + (r >> 2) * 8 + lrow + (r & 3);
+                            *(float*)(lds + band_off(row, col >> 2) + (col & 3) * 4) = acc[fm][fn][r];
+                        }
+                    }
+            }
+            wait_lgkmcnt0();
+            __builtin_amdgcn_s_barrier();
+            const int64_t band_row0 = row0 + band * C::WTM;
+            // Chunk i of this thread: row i*RPI + w*RPW + lane/CPRW, chunk lane%CPRW.  The rows
+            // one wave instruction touches (RPW of them, consecutive, starting at an even row)
+            // share a shard, so the shard base is computed once per instruction, wave-uniform.
+            constexpr int RPW = 64 / CPRW, RPI = C::NT / CPRW;
+            const int lrow_off = lane / CPRW, lchunk = lane % CPRW;
+            f32x4_t cur[PER_T];
+            float* rbase[PER_T];
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int64_t wrow = band_row0 + i * RPI + w * RPW;  // wave-uniform
+                rbase[i] = nullptr;
+                if (wrow < M) {
+                    const int s = p.num_shards == 1 ? 0 : (int)(wrow / p.shard_rows);
+                    rbase[i] = pick(p.d_ptr, s) + (wrow - (int64_t)s * p.shard_rows) * p.ldd + col0;
+                }
+            }
+            const int64_t loff = (int64_t)lrow_off * p.ldd + lchunk * 4;
+            const bool col_ok = col0 + lchunk * 4 < N;
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int64_t grow = band_row0 + i * RPI + w * RPW + lrow_off;
+                if (rbase[i] && grow < M && col_ok) cur[i] = *(const f32x4_t*)(rbase[i] + loff);
+            }
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int row = i * RPI + w * RPW + lrow_off;
+                const int64_t grow = band_row0 + row;
+                if (rbase[i] && grow < M && col_ok) {
+                    const f32x4_t a = *(const f32x4_t*)(lds + band_off(row, lchunk));
+                    *(f32x4_t*)(rbase[i] + loff) = cur[i] + a;
+                }
+            }
+        }
     } else {
-        // Reduction into the destination.  With several shards, shard_rows is a multiple of 32
-        // and tile rows start at multiples of 32, so every 32-row accumulator block lies in one
-        // shard and its destination base is uniform across the wave.
+        // Reduction into the destination with fp32 atomics.  With several shards, shard_rows is a
+        // multiple of 32 and tile rows start at multiples of 32, so every 32-row accumulator
+        // block lies in one shard and its destination base is uniform across the wave.
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             const int64_t brow = wrow0 + fm * 32;  // first row of this 32-row block
             if (brow < M) {
                 const int s = p.num_shards == 1 ? 0 : (int)(brow / p.shard_rows);
                 float* const dbase = pick(p.d_ptr, s) + (brow - (int64_t)s * p.shard_rows) * p.ldd;
-                if constexpr (EPI == EPI_OWNER_F32) {
-                    // read the whole destination block first, then add and write it back
-                    float cur[C::FN][16];
 #pragma unroll
-                    for (int fn = 0; fn < C::FN; ++fn) {
-                        const int64_t col = wcol0 + fn * 32 + lcol;
+                for (int fn = 0; fn < C::FN; ++fn) {
+                    const int64_t col = wcol0 + fn * 32 + lcol;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int rr = (r >> 2) * 8 + lrow + (r & 3);
-                            const bool in = (brow + rr < M) && (col < N);
-                            cur[fn][r] = in ? dbase[(int64_t)rr * p.ldd + col] : 0.0f;
-                        }
-                    }
-#pragma unroll
-                    for (int fn = 0; fn < C::FN; ++fn) {
-                        const int64_t col = wcol0 + fn * 32 + lcol;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int rr = (r >> 2) * 8 + lrow + (r & 3);
-                            if ((brow + rr < M) && (col < N))
-                                dbase[(int64_t)rr * p.ldd + col] = cur[fn][r] + acc[fm][fn][r];
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int fn = 0; fn < C::FN; ++fn) {
-                        const int64_t col = wcol0 + fn * 32 + lcol;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int rr = (r >> 2) * 8 + lrow + (r & 3);
-                            if ((brow + rr < M) && (col < N))
-                                __hip_atomic_fetch_add(dbase + (int64_t)rr * p.ldd + col,
-                                                       acc[fm][fn][r], __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = (r >> 2) * 8 + lrow + (r & 3);
+                        if ((brow + rr < M) && (col < N))
+                            __hip_atomic_fetch_add(dbase + (int64_t)rr * p.ldd + col,
+                                                   acc[fm][fn][r], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
             }
@@ -413,7 +502,6 @@ static hipError_t launch_cfg(const GemmArgs& a, TileCfgId cfg, Epi epi, int64_t 
     switch (cfg) {
         case CFG_256x256: return launch_epi<Cfg256x256, GROUPED>(a, epi, tiles, stream);
         case CFG_256x128: return launch_epi<Cfg256x128, GROUPED>(a, epi, tiles, stream);
-        case CFG_256x128_2WG: return launch_epi<Cfg256x128x2, GROUPED>(a, epi, tiles, stream);
         case CFG_128x128: return launch_epi<Cfg128x128, GROUPED>(a, epi, tiles, stream);
         default: return hipErrorInvalidValue;
     }

@@ -18,11 +18,10 @@ enum Epi : int {
 
 // Tile shapes compiled into the library (see pk_gemm.hip for what each is used for).
 enum TileCfgId : int {
-    CFG_256x256 = 0,  // 4 waves of 128x128, BK 64, one workgroup per CU
-    CFG_256x128 = 1,  // 4 waves of 128x64, BK 64, one workgroup per CU
-    CFG_256x128_2WG = 2,  // 4 waves of 128x64, BK 32, two workgroups per CU
-    CFG_128x128 = 3,  // 4 waves of 64x64, BK 64
-    CFG_COUNT = 4
+    CFG_256x256 = 0,  // 8 waves of 128x64, BK 64, 2 LDS stages (128 KB)
+    CFG_256x128 = 1,  // 4 waves of 128x64, BK 64, 3 LDS stages (144 KB)
+    CFG_128x128 = 2,  // 4 waves of 64x64, BK 64, 2 LDS stages (64 KB)
+    CFG_COUNT = 3
 };
 
 struct GemmArgs {
