@@ -66,7 +66,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(torch):
+    """A plain device-to-device copy of a known size: the HBM byte counters of a profiler run of
+    this mode give the scale factor between counter readings and bytes moved."""
+    n = 64 * 1024 * 1024  # 256 MiB of fp32
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                      "launches": 5}), flush=True)
 
 
 class Timer:
@@ -219,6 +234,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     name = args.workload
     res = run_gpu(name, args.mode, args.steps, args.warmup, torch, pk)
     tflops = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12

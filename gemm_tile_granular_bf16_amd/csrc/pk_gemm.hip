@@ -42,9 +42,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define PK_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int ST_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int ST_, int WG_PER_CU_ = 1>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, ST = ST_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, ST = ST_, WG_PER_CU = WG_PER_CU_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -57,21 +57,23 @@ struct Cfg {
     static constexpr int LPS = AI + BI;                  // DMA instructions per wave per step
     static constexpr int CPRA = BK / 8, CPRB = BN / 8;   // 16-byte chunks per LDS row
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA blocks");
-    static_assert(BK == 64, "A swizzle defined for 128-byte rows");
+    static_assert(BK == 64 || BK == 32, "A swizzle defined for 128- and 64-byte rows");
     static_assert(CPRB >= 16, "B swizzle needs at least 16 chunks per row");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 MFMA blocks");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS is 160 KB per CU");
+    static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS is 160 KB per CU");
     static_assert(ST >= 2 && ST <= 3, "pipeline depth");
 };
 
-using Cfg256x256 = Cfg<256, 256, 64, 2, 4, 2>;  // 8 waves of 128x64, 128 KB LDS
-using Cfg256x128 = Cfg<256, 128, 64, 2, 2, 3>;  // 4 waves of 128x64, 144 KB LDS
-using Cfg128x128 = Cfg<128, 128, 64, 2, 2, 2>;  // 4 waves of 64x64, 64 KB LDS
+using Cfg256x256 = Cfg<256, 256, 64, 2, 4, 2>;     // 8 waves of 128x64, 128 KB LDS
+using Cfg256x128 = Cfg<256, 128, 64, 2, 2, 3>;     // 4 waves of 128x64, 144 KB LDS
+using Cfg128x128 = Cfg<128, 128, 64, 2, 2, 2>;     // 4 waves of 64x64, 64 KB LDS
+using Cfg256x128x2 = Cfg<256, 128, 32, 2, 2, 3, 2>;  // 4 waves of 128x64, 72 KB LDS, 2 per CU
 
 TileShape tile_shape(TileCfgId cfg) {
     switch (cfg) {
         case CFG_256x256: return {256, 256};
         case CFG_256x128: return {256, 128};
+        case CFG_256x128_2WG: return {256, 128};
         default: return {128, 128};
     }
 }
@@ -80,7 +82,14 @@ TileShape tile_shape(TileCfgId cfg) {
 // Small device helpers
 // ------------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ int swz_a(int row) { return (row ^ (row >> 3)) & 7; }
+// A rows of 8 chunks (BK 64): chunk ^ (row ^ row>>3); of 4 chunks (BK 32): chunk ^ (row>>1 ^ row>>3).
+// Either way the 16 (or 8) consecutive rows one ds_read_b128 touches per bank cycle hit distinct
+// banks.
+template <int CPRA>
+__device__ __forceinline__ int swz_a(int row) {
+    if constexpr (CPRA == 8) return (row ^ (row >> 3)) & 7;
+    else return ((row >> 1) ^ (row >> 3)) & 3;
+}
 template <int CPRB>
 __device__ __forceinline__ int swz_b(int k) { return (10 * (k & 3)) & (CPRB - 1); }
 
@@ -132,7 +141,7 @@ __device__ __forceinline__ bool xcd_remap(int b, int total, int& L) {
 // ------------------------------------------------------------------------------------------------
 
 template <class C, bool GROUPED, int EPI>
-__global__ __launch_bounds__(C::NT, 1) void gemm_tile_kernel(GemmArgs p) {
+__global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_tile_kernel(GemmArgs p) {
     for (int j = 0; j < C::AI; ++j) {
         const int q = (j * C::NW + w) * 64 + lane;
         const int rl = q / C::CPRA;
-        const int c = (q % C::CPRA) ^ swz_a(rl);
+        const int c = (q % C::CPRA) ^ swz_a<C::CPRA>(rl);
         a_kc[j] = c * 8;
         int64_t r = row0 + rl;
         if (r >= row_end) r = row0;  // masked row: read a valid one, never stored
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(C::NT, 1) void gemm_tile_kernel(GemmArgs p) {
         const int r = wy * C::WTM + fm * 32 + (lane & 31);
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk)
-            a_off[fm][kk] = r * (C::BK * 2) + (((kk * 2 + (lane >> 5)) ^ swz_a(r)) << 4);
+            a_off[fm][kk] = r * (C::BK * 2) + (((kk * 2 + (lane >> 5)) ^ swz_a<C::CPRA>(r)) << 4);
     }
     // B operand of block fn, slice kk (two transposing reads, k rows +0..3 and +4..7):
     // in 16-lane group G, lane i reads row 8*(G/2) + i/4 (+4), columns n + 4*(i%4) .. +3 where
@@ -503,6 +512,7 @@ static hipError_t launch_cfg(const GemmArgs& a, TileCfgId cfg, Epi epi, int64_t 
         case CFG_256x256: return launch_epi<Cfg256x256, GROUPED>(a, epi, tiles, stream);
         case CFG_256x128: return launch_epi<Cfg256x128, GROUPED>(a, epi, tiles, stream);
         case CFG_128x128: return launch_epi<Cfg128x128, GROUPED>(a, epi, tiles, stream);
+        case CFG_256x128_2WG: return launch_epi<Cfg256x128x2, GROUPED>(a, epi, tiles, stream);
         default: return hipErrorInvalidValue;
     }
 }
