@@ -9,7 +9,12 @@
 // re-derived for CDNA4:
 //
 //  * MFMA v_mfma_f32_32x32x16_bf16: every wave owns an (FM*32) x (FN*32) accumulator block held
-//    in registers.
+//    in registers.  The A and B operand layouts of the instruction are mirror images (lane l holds
+//    8 consecutive k of line l % 32), so feeding the B fragment as the first operand computes the
+//    transposed block: lane l then holds row l % 32 of the tile and, in each group of 4 registers,
+//    4 consecutive columns, which the store and read-modify-write epilogues move as 16-byte
+//    vectors.  The atomic epilogue keeps the natural orientation (32 lanes on 32 consecutive
+//    columns of one row), which coalesces per-element atomics.
 //  * Operand staging without registers: both operands go HBM -> LDS with global_load_lds_dwordx4
 //    (each lane moves 16 bytes into its slot of a 1 KB wave-contiguous LDS block), so a whole
 //    stage is in flight while the previous one feeds the MFMAs.  A (M x K, k-contiguous) is
@@ -40,6 +45,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define PK_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int ST_, int WG_PER_CU_ = 1>
@@ -304,12 +310,18 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
             bfr[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
+    // Transposed blocks (row-contiguous lanes) for every epilogue except the atomic one.
+    constexpr bool ROWS_IN_LANES = EPI != EPI_ATOMIC_F32;
     auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+            for (int fn = 0; fn < C::FN; ++fn) {
+                if constexpr (ROWS_IN_LANES)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0);
+                else
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+            }
     };
 
     // ---- k-loop ---------------------------------------------------------------------------------
@@ -357,103 +369,126 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
     }
 
     // ---- epilogue ----------------------------------------------------------------------------
-    // Accumulator element r of block (fm, fn) in lane l sits at tile row
-    // fm*32 + (r/4)*8 + (l/32)*4 + r%4 and tile column fn*32 + l%32 of this wave's sub-tile.
-    const int lrow = (lane >> 5) * 4;
-    const int lcol = lane & 31;
     const int64_t wrow0 = row0 + wy * C::WTM;
     const int64_t wcol0 = col0 + wx * C::WTN;
 
     if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
+        // Registers 4g..4g+3 of block (fm, fn) in lane l: row fm*32 + l%32, columns
+        // fn*32 + 8g + 4*(l/32) + 0..3 of this wave's sub-tile.  N % 8 == 0, so a group of 4
+        // columns is entirely inside or entirely outside the matrix.
+        const int64_t lrow = wrow0 + (lane & 31);
+        const int64_t lcol = wcol0 + 4 * (lane >> 5);
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int64_t row = lrow + fm * 32;
+            if (row >= row_end) continue;
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
-                const int64_t col = wcol0 + fn * 32 + lcol;
+            for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = wrow0 + fm * 32 + (r >> 2) * 8 + lrow + (r & 3);
-                    if (row < row_end && col < N) {
-                        if constexpr (EPI == EPI_STORE_BF16)
-                            ((uint16_t*)p.C)[row * p.ldc + col] = (uint16_t)bf16_rne(acc[fm][fn][r]);
-                        else
-                            ((float*)p.C)[row * p.ldc + col] = acc[fm][fn][r];
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t col = lcol + fn * 32 + 8 * g;
+                    if (col >= N) continue;
+                    const f32x4_t v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1],
+                                       acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]};
+                    if constexpr (EPI == EPI_STORE_BF16) {
+                        u32x2 pk2;
+                        pk2[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+                        pk2[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+                        *(u32x2*)((uint16_t*)p.C + row * p.ldc + col) = pk2;
+                    } else {
+                        *(f32x4_t*)((float*)p.C + row * p.ldc + col) = v;
                     }
                 }
-            }
+        }
     } else if constexpr (EPI == EPI_OWNER_F32) {
-        // Owner-exclusive read-modify-write, staged through LDS (free after the k-loop): the
-        // tile is handled in WAVES_M bands of WTM rows.  The waves owning a band write their
-        // accumulators into LDS (fp32, row-major, 16-byte chunks XOR-swizzled so that rows 4
-        // apart use the other half of the banks); then every wave streams the band against the
-        // destination with 16-byte loads and stores, one destination row per wave instruction,
-        // all of a lane's loads in flight before the first add.
+        // Owner-exclusive read-modify-write, staged through LDS (free after the k-loop) so that
+        // the destination is touched with whole-row 16-byte vectors.  The tile is handled in
+        // WAVES_M bands of WTM rows.  Per band: every wave first issues the destination loads of
+        // its share of the band (streaming loads: the destination is touched once, so it should
+        // not push the operand panels out of the caches), the waves owning the band write their
+        // accumulators into LDS as 16-byte vectors (fp32 rows of BN; the 16-byte chunk index is
+        // XORed with row % 16, which spreads the 16 rows of one write phase over all banks), and
+        // after a barrier every wave adds the LDS rows to its loaded values and stores them.
+        // Loads use clamped, always-valid addresses and only the stores are predicated, so the
+        // loads of a band stay in flight together.
         constexpr int ROWB = C::BN * 4;                 // bytes per LDS row
-        constexpr int CHUNKS = C::WTM * C::BN / 4;      // 16-byte chunks per band
+        constexpr int CPRW = C::BN / 4;                 // 16-byte chunks per row
+        constexpr int CHUNKS = C::WTM * CPRW;           // chunks per band
         constexpr int PER_T = CHUNKS / C::NT;           // chunks per thread per band
-        constexpr int CPRW = C::BN / 4;                 // chunks per row
         static_assert(C::WTM * ROWB <= C::LDS_BYTES, "band must fit in LDS");
-        static_assert(CHUNKS % C::NT == 0 && C::NT % CPRW == 0, "whole rows per wave");
-        auto band_off = [&](int row, int chunk) {
-            return row * ROWB + ((chunk ^ (((row >> 2) & 1) << 3)) << 4);
-        };
+        static_assert(CHUNKS % C::NT == 0 && C::NT % CPRW == 0 && 64 % CPRW == 0, "whole rows per wave");
+        static_assert(CPRW >= 16, "swizzle needs 16 chunks per row");
+        auto stage_off = [&](int row, int chunk) { return row * ROWB + ((chunk ^ (row & 15)) << 4); };
+        // Chunk i of this thread: band row i*RPI + w*RPW + lane/CPRW, chunk lane%CPRW.
+        constexpr int RPW = 64 / CPRW, RPI = C::NT / CPRW;
+        const int lrow_off = lane / CPRW, lchunk = lane % CPRW;
+        const bool col_ok = col0 + lchunk * 4 < N;
+        const int lcol = col_ok ? lchunk * 4 : 0;  // clamped column for the loads
+        const int64_t shard_rows = p.num_shards == 1 ? M : p.shard_rows;
 #pragma unroll
         for (int band = 0; band < C::WAVES_M; ++band) {
-            wait_lgkmcnt0();
-            __builtin_amdgcn_s_barrier();
-            if (wy == band) {
-#pragma unroll
-                for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < C::FN; ++fn) {
-                        const int col = wx * C::WTN + fn * 32 + lcol;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int row = fm * 32 + (r >> 2) * 8 + lrow + (r & 3);
-                            *(float*)(lds + band_off(row, col >> 2) + (col & 3) * 4) = acc[fm][fn][r];
-                        }
-                    }
-            }
-            wait_lgkmcnt0();
-            __builtin_amdgcn_s_barrier();
             const int64_t band_row0 = row0 + band * C::WTM;
-            // Chunk i of this thread: row i*RPI + w*RPW + lane/CPRW, chunk lane%CPRW.  The rows
-            // one wave instruction touches (RPW of them, consecutive, starting at an even row)
-            // share a shard, so the shard base is computed once per instruction, wave-uniform.
-            constexpr int RPW = 64 / CPRW, RPI = C::NT / CPRW;
-            const int lrow_off = lane / CPRW, lchunk = lane % CPRW;
-            f32x4_t cur[PER_T];
-            float* rbase[PER_T];
+            if (band_row0 >= M) break;  // uniform across the workgroup
+            const int64_t band_last = min(band_row0 + C::WTM, M) - 1;
+            // Destination row pointers: one shard for the whole band (always with a single
+            // shard), else one division per row.
+            const int s0 = p.num_shards == 1 ? 0 : (int)(band_row0 / shard_rows);
+            const bool one_shard = p.num_shards == 1 || band_last / shard_rows == s0;
+            const int last_row = (int)(band_last - band_row0);
+            auto rmw_band = [&](auto row_ptr) {
+                f32x4_t cur[PER_T];
 #pragma unroll
-            for (int i = 0; i < PER_T; ++i) {
-                const int64_t wrow = band_row0 + i * RPI + w * RPW;  // wave-uniform
-                rbase[i] = nullptr;
-                if (wrow < M) {
-                    const int s = p.num_shards == 1 ? 0 : (int)(wrow / p.shard_rows);
-                    rbase[i] = pick(p.d_ptr, s) + (wrow - (int64_t)s * p.shard_rows) * p.ldd + col0;
+                for (int i = 0; i < PER_T; ++i) {
+                    const int row = min(i * RPI + w * RPW + lrow_off, last_row);
+                    cur[i] = __builtin_nontemporal_load((const f32x4_t*)(row_ptr(row) + lcol));
                 }
-            }
-            const int64_t loff = (int64_t)lrow_off * p.ldd + lchunk * 4;
-            const bool col_ok = col0 + lchunk * 4 < N;
+                // every wave is done reading LDS (the last k-step's operands, or the previous band)
+                wait_lgkmcnt0();
+                __builtin_amdgcn_s_barrier();
+                if (wy == band) {
 #pragma unroll
-            for (int i = 0; i < PER_T; ++i) {
-                const int64_t grow = band_row0 + i * RPI + w * RPW + lrow_off;
-                if (rbase[i] && grow < M && col_ok) cur[i] = *(const f32x4_t*)(rbase[i] + loff);
-            }
+                    for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-            for (int i = 0; i < PER_T; ++i) {
-                const int row = i * RPI + w * RPW + lrow_off;
-                const int64_t grow = band_row0 + row;
-                if (rbase[i] && grow < M && col_ok) {
-                    const f32x4_t a = *(const f32x4_t*)(lds + band_off(row, lchunk));
-                    *(f32x4_t*)(rbase[i] + loff) = cur[i] + a;
+                        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const int row = fm * 32 + (lane & 31);
+                                const int col = wx * C::WTN + fn * 32 + 8 * g + 4 * (lane >> 5);
+                                const f32x4_t v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1],
+                                                   acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]};
+                                *(f32x4_t*)(lds + stage_off(row, col >> 2)) = v;
+                            }
                 }
+                wait_lgkmcnt0();
+                __builtin_amdgcn_s_barrier();
+#pragma unroll
+                for (int i = 0; i < PER_T; ++i) {
+                    const int row = i * RPI + w * RPW + lrow_off;
+                    const f32x4_t a = *(const f32x4_t*)(lds + stage_off(row, lchunk));
+                    if (row <= last_row && col_ok) *(f32x4_t*)(row_ptr(row) + lchunk * 4) = cur[i] + a;
+                }
+            };
+            if (one_shard) {
+                // the whole band in one shard (always the case with a single shard)
+                float* const base = pick(p.d_ptr, s0) + (band_row0 - (int64_t)s0 * shard_rows) * p.ldd + col0;
+                const int64_t ldd = p.ldd;
+                rmw_band([=](int row) { return base + (int64_t)row * ldd; });
+            } else {
+                rmw_band([&](int row) {
+                    const int64_t grow = band_row0 + row;
+                    const int sh = (int)(grow / shard_rows);
+                    return pick(p.d_ptr, sh) + (grow - (int64_t)sh * shard_rows) * p.ldd + col0;
+                });
             }
         }
     } else {
-        // Reduction into the destination with fp32 atomics.  With several shards, shard_rows is a
-        // multiple of 32 and tile rows start at multiples of 32, so every 32-row accumulator
+        // Reduction into the destination with fp32 atomics (natural orientation: register r of
+        // block (fm, fn) in lane l is row fm*32 + (r/4)*8 + (l/32)*4 + r%4, column fn*32 + l%32,
+        // so 32 lanes cover 128 contiguous bytes of one row).  With several shards, shard_rows is
+        // a multiple of 32 and tile rows start at multiples of 32, so every 32-row accumulator
         // block lies in one shard and its destination base is uniform across the wave.
+        const int lrow = (lane >> 5) * 4;
+        const int lcol = lane & 31;
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             const int64_t brow = wrow0 + fm * 32;  // first row of this 32-row block
