@@ -35,6 +35,8 @@
 //  * Grid: workgroups are dealt round-robin to the 8 XCDs; block ids are remapped so that each
 //    XCD works on one contiguous run of logical tiles, and logical tiles are rastered in groups
 //    of tile rows, so operand panels are reused from that XCD's L2.
+#include <type_traits>
+
 #include "pk_internal.h"
 
 namespace pk {
@@ -330,42 +332,78 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
     auto stage_in = [&](int64_t kt, int slot) {
         if (ragged && kt == nk - 1) issue_tail(kt, slot); else issue(kt, slot);
     };
-    // vmcnt wait so that step `st` has landed, given DMAs issued for steps <= last
-    auto wait_step = [&](int64_t st, int64_t last) {
-        if constexpr (C::ST >= 3) {
-            if (last - st >= 1) { wait_vmcnt<C::LPS>(); return; }
-        }
-        wait_vmcnt<0>();
-    };
     if (nk > 0) {
+        // prologue: steps 0 .. ST-2 in flight, wait for step 0, then refill with step ST-1
 #pragma unroll
         for (int s = 0; s < C::ST - 1; ++s)
             if (s < nk) stage_in(s, s);
-        int64_t last = nk - 1 < C::ST - 2 ? nk - 1 : C::ST - 2;
         wait_lgkmcnt0();
-        wait_step(0, last);
+        if constexpr (C::ST >= 3) {
+            if (nk >= 2) wait_vmcnt<C::LPS * (C::ST - 2)>(); else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
         __builtin_amdgcn_s_barrier();
-        if (C::ST - 1 < nk) { stage_in(C::ST - 1, C::ST - 1); last = C::ST - 1; }
+        if (C::ST - 1 < nk) stage_in(C::ST - 1, C::ST - 1);
         bf16x8 fa[2][C::FM], fb[2][C::FN];
         read_frags(0, 0, fa[0], fb[0]);
-        for (int64_t kt = 0; kt < nk; ++kt) {
+        // One k-step: the MFMAs of slice kk are interleaved with the LDS reads of slice kk+1
+        // (one read per MFMA, pinned with scheduling-group barriers).  At the last slice the wave
+        // waits for its own reads and for step kt+1 to land, meets the others at the barrier,
+        // refills the slot every wave has finished with, and reads slice 0 of step kt+1, all
+        // interleaved with the MFMAs of the last slice.  Modes: MODE_ISSUE refills with a full
+        // step, MODE_TAIL with the ragged last step, MODE_DRAIN refills nothing, MODE_LAST has
+        // no step after it.  The steady-state loop has no branches.
+        constexpr int MODE_ISSUE = 0, MODE_TAIL = 1, MODE_DRAIN = 2, MODE_LAST = 3;
+        constexpr int NR = C::FM + 2 * C::FN;  // LDS reads per k16 slice
+        constexpr int NM = C::FM * C::FN;      // MFMAs per k16 slice
+        auto step = [&](int64_t kt, auto mode_c) {
+            constexpr int MODE = decltype(mode_c)::value;
             const int slot = (int)(kt % C::ST);
 #pragma unroll
             for (int kk = 0; kk < C::KK; ++kk) {
                 const int nb = (kk + 1) & 1;
                 if (kk + 1 < C::KK) {
                     read_frags(slot, kk + 1, fa[nb], fb[nb]);
-                } else if (kt + 1 < nk) {
-                    // this wave's reads of step kt are complete, step kt+1 has landed everywhere
+                    mfmas(fa[kk & 1], fb[kk & 1]);
+#pragma unroll
+                    for (int i = 0; i < NM; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    }
+                } else if constexpr (MODE != MODE_LAST) {
                     wait_lgkmcnt0();
-                    wait_step(kt + 1, last);
+                    if constexpr (C::ST >= 3) {
+                        // a later step than kt+1 is in flight unless kt+1 is the last one
+                        if (MODE != MODE_DRAIN || kt + 2 < nk) wait_vmcnt<C::LPS>(); else wait_vmcnt<0>();
+                    } else {
+                        wait_vmcnt<0>();
+                    }
                     __builtin_amdgcn_s_barrier();
-                    if (kt + C::ST < nk) { stage_in(kt + C::ST, (int)((kt + C::ST) % C::ST)); last = kt + C::ST; }
+                    if constexpr (MODE == MODE_ISSUE) issue(kt + C::ST, slot);
+                    if constexpr (MODE == MODE_TAIL) issue_tail(kt + C::ST, slot);
                     read_frags((int)((kt + 1) % C::ST), 0, fa[nb], fb[nb]);
+                    mfmas(fa[kk & 1], fb[kk & 1]);
+                    if constexpr (MODE == MODE_ISSUE) {
+#pragma unroll
+                        for (int i = 0; i < NM; ++i) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            if (i < C::LPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
+                            if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        }
+                    }
+                } else {
+                    mfmas(fa[kk & 1], fb[kk & 1]);
                 }
-                mfmas(fa[kk & 1], fb[kk & 1]);
             }
-        }
+        };
+        // steps [0, nk_full) are whole BK slices; a ragged last step is staged by issue_tail
+        const int64_t nk_full = ragged ? nk - 1 : nk;
+        int64_t kt = 0;
+        for (; kt + C::ST < nk_full; ++kt) step(kt, std::integral_constant<int, MODE_ISSUE>{});
+        if (ragged && kt + C::ST == nk - 1) { step(kt, std::integral_constant<int, MODE_TAIL>{}); ++kt; }
+        for (; kt + 1 < nk; ++kt) step(kt, std::integral_constant<int, MODE_DRAIN>{});
+        step(kt, std::integral_constant<int, MODE_LAST>{});
     }
 
     // ---- epilogue ----------------------------------------------------------------------------
