@@ -127,10 +127,11 @@ def setup_workload(name, mode, torch, pk):
                 pk.gemm_reduce(a, b, shards, mode=mode_id,
                                out_bf16=out if (out is not None and i == len(ops) - 1) else None)
         flops = w.flops
-        # A and B once, destination read + written once per producer, cast read + write
+        # A and B once, destination read + written once per producer; the bf16 output is written
+        # by the owner epilogue (2 B per element) or by a cast pass that re-reads the destination
         nbytes = sum(2 * (w.M * w.K + w.K * w.N) + 8 * w.M * w.N for _ in prods)
         if w.cast_bf16:
-            nbytes += 6 * w.M * w.N
+            nbytes += (2 if mode == "owner" else 6) * w.M * w.N
         desc = {"M": w.M, "N": w.N, "K": w.K, "producers": w.producers, "shards": w.shards,
                 "prefill_partials": w.prefill_partials, "reduce": mode,
                 "cast_bf16": w.cast_bf16}

@@ -158,10 +158,17 @@ pk_status pk_gemm_reduce(int64_t M, int64_t N, int64_t K, const uint16_t* A, int
         a.num_shards = num_shards;
         a.ldd = ldd;
         a.group_m = 8;
-        const pk::Epi epi = mode == PK_REDUCE_ATOMIC ? pk::EPI_ATOMIC_F32 : pk::EPI_OWNER_F32;
+        // Owner mode writes the bf16 output from the epilogue (the destination has one writer, so
+        // the updated value is final); atomic mode casts in a pass after the reduction.
+        const bool fused_cast = out_bf16 && mode == PK_REDUCE_OWNER;
+        if (fused_cast) { a.C = out_bf16; a.ldc = ldo; }
+        const pk::Epi epi = mode == PK_REDUCE_ATOMIC ? pk::EPI_ATOMIC_F32
+                            : fused_cast             ? pk::EPI_OWNER_CAST
+                                                     : pk::EPI_OWNER_F32;
         pk_status st = hip_status(pk::launch_gemm(a, pick_reduce_cfg(M, N), epi, s),
                                   "pk_gemm_reduce launch");
         if (st != PK_OK) return st;
+        if (fused_cast) return ok();
     }
     if (out_bf16)
         return hip_status(pk::launch_cast(D_shards, num_shards, shard_rows, ldd, M, N, out_bf16,

@@ -438,7 +438,7 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
                     }
                 }
         }
-    } else if constexpr (EPI == EPI_OWNER_F32) {
+    } else if constexpr (EPI == EPI_OWNER_F32 || EPI == EPI_OWNER_CAST) {
         // Owner-exclusive read-modify-write, staged through LDS (free after the k-loop) so that
         // the destination is touched with whole-row 16-byte vectors.  The tile is handled in
         // WAVES_M bands of WTM rows.  Per band: every wave first issues the destination loads of
@@ -448,7 +448,9 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
         // XORed with row % 16, which spreads the 16 rows of one write phase over all banks), and
         // after a barrier every wave adds the LDS rows to its loaded values and stores them.
         // Loads use clamped, always-valid addresses and only the stores are predicated, so the
-        // loads of a band stay in flight together.
+        // loads of a band stay in flight together.  EPI_OWNER_CAST also writes the bf16 rounding
+        // of every updated value to C: with a single writer of the destination that is the
+        // final value, so the all-reduce output needs no second pass over the destination.
         constexpr int ROWB = C::BN * 4;                 // bytes per LDS row
         constexpr int CPRW = C::BN / 4;                 // 16-byte chunks per row
         constexpr int CHUNKS = C::WTM * CPRW;           // chunks per band
@@ -503,7 +505,16 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
                 for (int i = 0; i < PER_T; ++i) {
                     const int row = i * RPI + w * RPW + lrow_off;
                     const f32x4_t a = *(const f32x4_t*)(lds + stage_off(row, lchunk));
-                    if (row <= last_row && col_ok) *(f32x4_t*)(row_ptr(row) + lchunk * 4) = cur[i] + a;
+                    const f32x4_t nv = cur[i] + a;
+                    if (row <= last_row && col_ok) {
+                        *(f32x4_t*)(row_ptr(row) + lchunk * 4) = nv;
+                        if constexpr (EPI == EPI_OWNER_CAST) {
+                            u32x2 pk2;
+                            pk2[0] = bf16_rne(nv[0]) | (bf16_rne(nv[1]) << 16);
+                            pk2[1] = bf16_rne(nv[2]) | (bf16_rne(nv[3]) << 16);
+                            *(u32x2*)((uint16_t*)p.C + (band_row0 + row) * p.ldc + col0 + lchunk * 4) = pk2;
+                        }
+                    }
                 }
             };
             if (one_shard) {
@@ -573,6 +584,9 @@ static hipError_t launch_epi(const GemmArgs& a, Epi epi, int64_t tiles, hipStrea
             break;
         case EPI_OWNER_F32:
             if constexpr (!GROUPED) return launch_one<C, false, EPI_OWNER_F32>(a, tiles, stream);
+            break;
+        case EPI_OWNER_CAST:
+            if constexpr (!GROUPED) return launch_one<C, false, EPI_OWNER_CAST>(a, tiles, stream);
             break;
     }
     return hipErrorInvalidValue;

@@ -13,7 +13,8 @@ enum Epi : int {
     EPI_STORE_BF16 = 0,  // C = bf16(acc), round to nearest even
     EPI_STORE_F32 = 1,   // C = acc
     EPI_ATOMIC_F32 = 2,  // D += acc, one fp32 atomic add per element
-    EPI_OWNER_F32 = 3    // D += acc, owner-exclusive vector read-modify-write
+    EPI_OWNER_F32 = 3,   // D += acc, owner-exclusive vector read-modify-write
+    EPI_OWNER_CAST = 4   // as EPI_OWNER_F32, and C = bf16(D + acc) (round to nearest even)
 };
 
 // Tile shapes compiled into the library (see pk_gemm.hip for what each is used for).

@@ -102,9 +102,12 @@ pk_status pk_gemm(int64_t M, int64_t N, int64_t K,
  * The shards must cover M exactly (num_shards == ceil(M / shard_rows), 1..PK_MAX_PARTS); with more
  * than one shard, shard_rows must be a multiple of 32 (PK_ERR_UNSUPPORTED otherwise).  `mode`
  * selects per-element fp32 atomics or the owner-exclusive read-modify-write (see pk_reduce_mode).
- * If out_bf16 != NULL, a cast pass follows on the same stream, after this call's reduction:
- * out_bf16[r*ldo + c] = bf16_round_nearest_even(D[r][c]) for every r < M, c < N (the all-reduce
- * output; the caller makes sure every other producer has finished by then).  K == 0 adds nothing.
+ * If out_bf16 != NULL, out_bf16[r*ldo + c] = bf16_round_nearest_even(D[r][c]) for every r < M,
+ * c < N, with D the destination after this call's reduction (the all-reduce output; the caller
+ * makes sure every other producer has finished by then).  In PK_REDUCE_OWNER mode the same kernel
+ * writes each rounded value right after updating it (the call is the destination's only writer,
+ * so that value is final); in PK_REDUCE_ATOMIC mode, and when K == 0, a cast pass over the
+ * destination follows on the same stream.  K == 0 adds nothing.
  */
 pk_status pk_gemm_reduce(int64_t M, int64_t N, int64_t K,
                          const uint16_t* A, int64_t lda,

@@ -117,6 +117,32 @@ def test_ragged_shards_and_padded_destination(pk, oracle_mod, mode):
     _check_reduce(got[:, :N], R, [(A, B)], D0, "ragged")
 
 
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_ragged_shards_with_bf16_output(pk, oracle_mod, mode):
+    """The all-reduce output on a ragged problem with several shards and padded leading
+    dimensions: in owner mode the epilogue writes it, in atomic mode a cast pass does.  Either way
+    every element must equal the oracle's rounding of the GPU's own fp32 destination, and the
+    padding of both buffers stays untouched."""
+    M, N, K = 1000, 136, 200
+    A = pk_inputs.normal_bf16((M, K), 1.0, 121)
+    B = pk_inputs.normal_bf16((K, N), 1.0, 122)
+    D0 = np.random.Generator(np.random.PCG64(123)).standard_normal((M, N)).astype(np.float32)
+    base = torch.zeros((M, 160), device="cuda")
+    base[:, :N] = torch.from_numpy(D0).cuda()
+    base[:, N:] = 5.0
+    shards = [base[r:r + 256, :N] for r in range(0, M, 256)]
+    out_base = torch.full((M, 144), 7.0, dtype=torch.bfloat16, device="cuda")
+    pk.gemm_reduce(dev_bf16(A), dev_bf16(B), shards, mode=mode, out_bf16=out_base[:, :N])
+    torch.cuda.synchronize()
+    got = host_f32(base)
+    assert np.all(got[:, N:] == 5.0)
+    R = oracle_mod.reduce(D0, [(A, B)])
+    _check_reduce(got[:, :N], R, [(A, B)], D0, "ragged+cast")
+    out = host_bits(out_base)
+    assert np.array_equal(out[:, :N], oracle_mod.cast_f32_bf16(np.ascontiguousarray(got[:, :N])))
+    assert np.all(out[:, N:] == 0x40e0)  # bf16 bits of 7.0
+
+
 def test_k_zero_adds_nothing_and_cast_still_runs(pk, oracle_mod):
     M, N = 96, 64
     D0 = np.random.Generator(np.random.PCG64(7)).standard_normal((M, N)).astype(np.float32)
