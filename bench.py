@@ -85,23 +85,28 @@ def calibrate_copy(torch):
 
 
 class Timer:
-    """Per-step HIP events recorded on the stream the kernels are launched on."""
+    """HIP events recorded on the stream the kernels are launched on: one before the first timed
+    step and one after the last, so the average device time per step carries no per-step event
+    overhead (back-to-back launches on one stream)."""
 
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
-        self.pairs = []
+        self.start = torch.cuda.Event(enable_timing=True)
+        self.end = torch.cuda.Event(enable_timing=True)
+        self.steps = 0
+
+    def begin(self):
+        self.start.record(self.stream)
 
     def step(self, fn):
-        t = self.torch
-        e0 = t.cuda.Event(enable_timing=True)
-        e1 = t.cuda.Event(enable_timing=True)
-        e0.record(self.stream)
         fn()
-        e1.record(self.stream)
-        self.pairs.append((e0, e1))
+        self.steps += 1
+
+    def finish(self):
+        self.end.record(self.stream)
 
     def kernel_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+        return self.start.elapsed_time(self.end) / max(self.steps, 1)
 
 
 def setup_workload(name, mode, torch, pk):
@@ -179,8 +184,10 @@ def run_gpu(name, mode, steps, warmup, torch, pk):
     torch.cuda.synchronize()
     timer = Timer(torch, stream)
     t0 = time.perf_counter()
+    timer.begin()
     for _ in range(steps):
         timer.step(step)
+    timer.finish()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kms = timer.kernel_ms()
