@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "pk_internal.h"
 
 namespace {
@@ -32,6 +34,37 @@ pk_status hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Compute units of the current device, queried once per device (0 if the query fails).
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Grouped product workspace: [dispatch plan words | finished-piece counters | partial tiles].
+constexpr pk::TileCfgId kGroupedCfg = pk::CFG_256x256;
+struct GroupedWorkspace {
+    size_t counters_off, partials_off, bytes;
+};
+GroupedWorkspace grouped_workspace(const pk::DispatchPlan& plan) {
+    const pk::TileShape t = pk::tile_shape(kGroupedCfg);
+    GroupedWorkspace w;
+    w.counters_off = align256(plan.ws_bytes);
+    w.partials_off = align256(w.counters_off + sizeof(int32_t) * pk::kSplitMaxPieces);
+    w.bytes = w.partials_off + sizeof(float) * (size_t)t.bm * t.bn * pk::kSplitMaxPieces;
+    return w;
+}
 
 // Tile shape for a dense product: big outputs use 256x256 tiles (one workgroup per CU); when that
 // leaves the 256 CUs under two tiles each, 256x128; small problems 128x128.
@@ -179,8 +212,7 @@ pk_status pk_gemm_reduce(int64_t M, int64_t N, int64_t K, const uint16_t* A, int
 
 size_t pk_grouped_gemm_workspace_size(int64_t T, int top_k, int num_local) {
     if (T < 0 || top_k < 1 || top_k > 64 || num_local < 1 || num_local > 1024) return 0;
-    const pk::DispatchPlan plan = pk::plan_dispatch(T, top_k, num_local);
-    return plan.ws_bytes;
+    return grouped_workspace(pk::plan_dispatch(T, top_k, num_local)).bytes;
 }
 
 pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num_experts,
@@ -200,9 +232,10 @@ pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num
     if (T > 0 && N > 0 && (!X || !W || !Y)) return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
     if (ldx < K || ldy < N) return fail(PK_ERR_INVALID_ARGUMENT, "leading dimension too small");
     const pk::DispatchPlan plan = pk::plan_dispatch(T, top_k, num_local);
-    if (workspace_bytes < plan.ws_bytes)
+    const GroupedWorkspace gw = grouped_workspace(plan);
+    if (workspace_bytes < gw.bytes)
         return fail(PK_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, need %zu", workspace_bytes,
-                    plan.ws_bytes);
+                    gw.bytes);
     if (K % 8 || N % 8) return fail(PK_ERR_UNSUPPORTED, "K and N must be multiples of 8");
     if (ldx % 8 || (y_dtype == PK_BF16 ? ldy % 8 : ldy % 4))
         return fail(PK_ERR_UNSUPPORTED, "leading dimensions must be 16-byte multiples");
@@ -210,13 +243,16 @@ pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num
         return fail(PK_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
 
     hipStream_t s = (hipStream_t)stream;
-    // workspace: [slice counts | tile offsets]
+    // workspace: [slice counts | tile offsets | counters | partial tiles]
     int32_t* slice_counts = (int32_t*)workspace;
     int32_t* tile_offsets = slice_counts + (size_t)plan.num_slices * num_local;
-    const pk::TileCfgId cfg = pk::CFG_256x256;
+    int32_t* counters = (int32_t*)((char*)workspace + gw.counters_off);
+    float* partials = (float*)((char*)workspace + gw.partials_off);
+    const pk::TileCfgId cfg = kGroupedCfg;
     const pk::TileShape t = pk::tile_shape(cfg);
     hipError_t e = pk::launch_dispatch(plan, topk_ids, num_experts, expert_begin, num_local, t.bm,
-                                       offsets, perm, tile_offsets, slice_counts, s);
+                                       offsets, perm, tile_offsets, slice_counts, counters,
+                                       pk::kSplitMaxPieces, s);
     if (e != hipSuccess) return hip_status(e, "pk_grouped_gemm dispatch launch");
     if (T == 0 || N == 0) return ok();
 
@@ -235,9 +271,17 @@ pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num
     a.B = W; a.ldb = N;
     a.b_stride = K * N;
     a.C = Y; a.ldc = ldy;
-    // sum_e ceil(count_e / BM) <= rows / BM + num_local, and rows <= T * top_k
+    a.partials = partials;
+    a.counters = counters;
+    // one workgroup per CU with this tile shape; at most kSplitMaxPieces pieces
+    int slots = device_cu_count();
+    if (slots > pk::kSplitMaxPieces) slots = pk::kSplitMaxPieces;
+    a.split_slots = slots > 0 ? slots : 0;
+    // sum_e ceil(count_e / BM) <= rows / BM + num_local, and rows <= T * top_k; the split tail
+    // adds at most kSplitMaxPieces blocks after the whole tiles (rounded up to 8)
     const int64_t rows_max = T * (int64_t)top_k;
-    const int64_t max_tiles = (rows_max / t.bm + num_local) * ceil_div(N, t.bn);
+    const int64_t max_tiles = (rows_max / t.bm + num_local) * ceil_div(N, t.bn) + 8 +
+                              pk::kSplitMaxPieces;
     const pk::Epi epi = y_dtype == PK_BF16 ? pk::EPI_STORE_BF16 : pk::EPI_STORE_F32;
     return hip_status(pk::launch_grouped(a, cfg, epi, max_tiles, s), "pk_grouped_gemm launch");
 }

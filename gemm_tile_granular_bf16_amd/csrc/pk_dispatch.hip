@@ -84,12 +84,14 @@ __global__ __launch_bounds__(64) void dispatch_count_kernel(const int32_t* ids, 
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int num_slices, int num_local,
                                                              int tile_m, int32_t* slice_counts,
                                                              int32_t* offsets,
-                                                             int32_t* tile_offsets) {
+                                                             int32_t* tile_offsets,
+                                                             int32_t* zero, int n_zero) {
     __shared__ int stage[kScanLds];
     __shared__ int tot[kMaxLocal];
     __shared__ int scan_a[kMaxLocal], scan_b[kMaxLocal];
     const int tid = threadIdx.x;
     const int n = num_slices * num_local;
+    for (int i = tid; i < n_zero; i += blockDim.x) zero[i] = 0;
     for (int i = tid; i < n; i += blockDim.x) stage[i] = slice_counts[i];
     __syncthreads();
     // running base of every slice inside each expert
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* ids
 hipError_t launch_dispatch(const DispatchPlan& plan, const int32_t* topk_ids, int num_experts,
                            int expert_begin, int num_local, int tile_m, int32_t* offsets,
                            int32_t* perm, int32_t* tile_offsets, int32_t* slice_counts,
-                           hipStream_t stream) {
+                           int32_t* zero, int n_zero, hipStream_t stream) {
     int key_bits = 0;
     while ((1 << key_bits) <= num_local) ++key_bits;  // keys 0..num_local
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(plan.num_slices), dim3(64), 0, stream,
@@ -170,7 +172,8 @@ hipError_t launch_dispatch(const DispatchPlan& plan, const int32_t* topk_ids, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, stream, plan.num_slices,
-                       num_local, tile_m, slice_counts, offsets, tile_offsets);
+                       num_local, tile_m, slice_counts, offsets, tile_offsets, zero,
+                       zero ? n_zero : 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(plan.num_slices), dim3(64), 0, stream,

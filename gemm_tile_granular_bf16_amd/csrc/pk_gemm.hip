@@ -76,12 +76,16 @@ using Cfg256x256 = Cfg<256, 256, 64, 2, 4, 2>;     // 8 waves of 128x64, 128 KB 
 using Cfg256x128 = Cfg<256, 128, 64, 2, 2, 3>;     // 4 waves of 128x64, 144 KB LDS
 using Cfg128x128 = Cfg<128, 128, 64, 2, 2, 2>;     // 4 waves of 64x64, 64 KB LDS
 using Cfg256x128x2 = Cfg<256, 128, 32, 2, 2, 3, 2>;  // 4 waves of 128x64, 72 KB LDS, 2 per CU
+using Cfg128x256 = Cfg<128, 256, 64, 2, 4, 3>;      // 8 waves of 64x64, 144 KB LDS
+using Cfg128x256w4 = Cfg<128, 256, 64, 1, 4, 3>;    // 4 waves of 128x64, 144 KB LDS
 
 TileShape tile_shape(TileCfgId cfg) {
     switch (cfg) {
         case CFG_256x256: return {256, 256};
         case CFG_256x128: return {256, 128};
         case CFG_256x128_2WG: return {256, 128};
+        case CFG_128x256: return {128, 256};
+        case CFG_128x256_4W: return {128, 256};
         default: return {128, 128};
     }
 }
@@ -165,10 +169,37 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
     int64_t row0, row_end, col0;
     const uint16_t* Bm = p.B;
     int L;
+    const int64_t nk = (K + C::BK - 1) / C::BK;
+    int64_t kt_begin = 0, kt_end = nk;  // k-steps this workgroup computes
+    int piece = -1, pieces = 1, piece_tile = 0;
     if constexpr (GROUPED) {
         const int num_local = p.num_local;
         const int mt_total = p.tile_offsets[num_local];
-        if (!xcd_remap(blockIdx.x, mt_total * tiles_n, L)) return;
+        const int total = mt_total * tiles_n;
+        // The tiles of the last partial round (total mod split_slots of them) are split into
+        // `pieces` k-ranges each, so that the round is filled: blocks [0, dpb) take whole tiles,
+        // the next tail * pieces blocks take one piece each (dispatched last).
+        int dp = total, tail = 0;
+        if (p.split_slots > 0 && total > 0) {
+            const int r = total % p.split_slots;
+            int sp = r > 0 ? p.split_slots / r : 0;
+            if (sp > kSplitMaxPerTile) sp = kSplitMaxPerTile;
+            if (sp > nk) sp = (int)nk;
+            if (sp >= 2) { tail = r; pieces = sp; dp = total - r; }
+        }
+        const int dpb = (dp + 7) & ~7;
+        if ((int)blockIdx.x < dpb) {
+            if (!xcd_remap(blockIdx.x, dp, L)) return;
+            pieces = 1;
+        } else {
+            const int q = (int)blockIdx.x - dpb;
+            if (q >= tail * pieces) return;
+            piece_tile = q / pieces;
+            piece = q - piece_tile * pieces;
+            L = dp + piece_tile;
+            kt_begin = (int64_t)piece * nk / pieces;  // balanced: every piece has a k-step
+            kt_end = (int64_t)(piece + 1) * nk / pieces;
+        }
         // expert e: largest e with tile_offsets[e] * tiles_n <= L (empty experts are skipped)
         int lo = 0, hi = num_local;
         while (hi - lo > 1) {
@@ -327,39 +358,42 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
     };
 
     // ---- k-loop ---------------------------------------------------------------------------------
-    const int64_t nk = (K + C::BK - 1) / C::BK;
+    // Local steps j = 0 .. nkl-1 are global k-steps kt_begin + j (the whole K unless this block is
+    // one piece of a split tile); LDS slot j % ST.
     const bool ragged = (K % C::BK) != 0;
-    auto stage_in = [&](int64_t kt, int slot) {
-        if (ragged && kt == nk - 1) issue_tail(kt, slot); else issue(kt, slot);
+    const int64_t nkl = kt_end - kt_begin;
+    const bool tail_here = ragged && kt_end == nk;  // the ragged global last step is ours
+    auto stage_in = [&](int64_t j, int slot) {
+        if (tail_here && j == nkl - 1) issue_tail(kt_begin + j, slot); else issue(kt_begin + j, slot);
     };
-    if (nk > 0) {
+    if (nkl > 0) {
         // prologue: steps 0 .. ST-2 in flight, wait for step 0, then refill with step ST-1
 #pragma unroll
-        for (int s = 0; s < C::ST - 1; ++s)
-            if (s < nk) stage_in(s, s);
+        for (int st = 0; st < C::ST - 1; ++st)
+            if (st < nkl) stage_in(st, st);
         wait_lgkmcnt0();
         if constexpr (C::ST >= 3) {
-            if (nk >= 2) wait_vmcnt<C::LPS * (C::ST - 2)>(); else wait_vmcnt<0>();
+            if (nkl >= 2) wait_vmcnt<C::LPS * (C::ST - 2)>(); else wait_vmcnt<0>();
         } else {
             wait_vmcnt<0>();
         }
         __builtin_amdgcn_s_barrier();
-        if (C::ST - 1 < nk) stage_in(C::ST - 1, C::ST - 1);
+        if (C::ST - 1 < nkl) stage_in(C::ST - 1, C::ST - 1);
         bf16x8 fa[2][C::FM], fb[2][C::FN];
         read_frags(0, 0, fa[0], fb[0]);
         // One k-step: the MFMAs of slice kk are interleaved with the LDS reads of slice kk+1
         // (one read per MFMA, pinned with scheduling-group barriers).  At the last slice the wave
-        // waits for its own reads and for step kt+1 to land, meets the others at the barrier,
-        // refills the slot every wave has finished with, and reads slice 0 of step kt+1, all
+        // waits for its own reads and for step j+1 to land, meets the others at the barrier,
+        // refills the slot every wave has finished with, and reads slice 0 of step j+1, all
         // interleaved with the MFMAs of the last slice.  Modes: MODE_ISSUE refills with a full
         // step, MODE_TAIL with the ragged last step, MODE_DRAIN refills nothing, MODE_LAST has
         // no step after it.  The steady-state loop has no branches.
         constexpr int MODE_ISSUE = 0, MODE_TAIL = 1, MODE_DRAIN = 2, MODE_LAST = 3;
         constexpr int NR = C::FM + 2 * C::FN;  // LDS reads per k16 slice
         constexpr int NM = C::FM * C::FN;      // MFMAs per k16 slice
-        auto step = [&](int64_t kt, auto mode_c) {
+        auto step = [&](int64_t j, auto mode_c) {
             constexpr int MODE = decltype(mode_c)::value;
-            const int slot = (int)(kt % C::ST);
+            const int slot = (int)(j % C::ST);
 #pragma unroll
             for (int kk = 0; kk < C::KK; ++kk) {
                 const int nb = (kk + 1) & 1;
@@ -374,15 +408,15 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
                 } else if constexpr (MODE != MODE_LAST) {
                     wait_lgkmcnt0();
                     if constexpr (C::ST >= 3) {
-                        // a later step than kt+1 is in flight unless kt+1 is the last one
-                        if (MODE != MODE_DRAIN || kt + 2 < nk) wait_vmcnt<C::LPS>(); else wait_vmcnt<0>();
+                        // a later step than j+1 is in flight unless j+1 is the last one
+                        if (MODE != MODE_DRAIN || j + 2 < nkl) wait_vmcnt<C::LPS>(); else wait_vmcnt<0>();
                     } else {
                         wait_vmcnt<0>();
                     }
                     __builtin_amdgcn_s_barrier();
-                    if constexpr (MODE == MODE_ISSUE) issue(kt + C::ST, slot);
-                    if constexpr (MODE == MODE_TAIL) issue_tail(kt + C::ST, slot);
-                    read_frags((int)((kt + 1) % C::ST), 0, fa[nb], fb[nb]);
+                    if constexpr (MODE == MODE_ISSUE) issue(kt_begin + j + C::ST, slot);
+                    if constexpr (MODE == MODE_TAIL) issue_tail(kt_begin + j + C::ST, slot);
+                    read_frags((int)((j + 1) % C::ST), 0, fa[nb], fb[nb]);
                     mfmas(fa[kk & 1], fb[kk & 1]);
                     if constexpr (MODE == MODE_ISSUE) {
 #pragma unroll
@@ -397,13 +431,62 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
                 }
             }
         };
-        // steps [0, nk_full) are whole BK slices; a ragged last step is staged by issue_tail
-        const int64_t nk_full = ragged ? nk - 1 : nk;
-        int64_t kt = 0;
-        for (; kt + C::ST < nk_full; ++kt) step(kt, std::integral_constant<int, MODE_ISSUE>{});
-        if (ragged && kt + C::ST == nk - 1) { step(kt, std::integral_constant<int, MODE_TAIL>{}); ++kt; }
-        for (; kt + 1 < nk; ++kt) step(kt, std::integral_constant<int, MODE_DRAIN>{});
-        step(kt, std::integral_constant<int, MODE_LAST>{});
+        // local steps [0, nkl_full) are whole BK slices; a ragged last step is staged by issue_tail
+        const int64_t nkl_full = tail_here ? nkl - 1 : nkl;
+        int64_t j = 0;
+        for (; j + C::ST < nkl_full; ++j) step(j, std::integral_constant<int, MODE_ISSUE>{});
+        if (tail_here && j + C::ST == nkl - 1) { step(j, std::integral_constant<int, MODE_TAIL>{}); ++j; }
+        for (; j + 1 < nkl; ++j) step(j, std::integral_constant<int, MODE_DRAIN>{});
+        step(j, std::integral_constant<int, MODE_LAST>{});
+    }
+
+    if constexpr (GROUPED) {
+        if (piece >= 0) {
+            // One piece of a split tile: store the fp32 partial tile (this layout, 16-byte
+            // vectors), publish it, and count the piece.  The piece that completes the count adds
+            // the other pieces' partials into its registers and goes on to the normal epilogue;
+            // the others are done.  No block waits for another.
+            float* const part = p.partials + (int64_t)(piece_tile * pieces) * (C::BM * C::BN);
+            const int prow = wy * C::WTM + (lane & 31);
+            const int pcol = wx * C::WTN + 4 * (lane >> 5);
+            auto part_at = [&](int q, int fm, int fn, int g) {
+                return (f32x4_t*)(part + (int64_t)q * (C::BM * C::BN) +
+                                  (prow + fm * 32) * C::BN + pcol + fn * 32 + 8 * g);
+            };
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *part_at(piece, fm, fn, g) = f32x4_t{acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1],
+                                                            acc[fm][fn][4 * g + 2], acc[fm][fn][4 * g + 3]};
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            __shared__ int done_before;
+            if (tid == 0)
+                done_before = __hip_atomic_fetch_add(p.counters + piece_tile, 1, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (done_before != pieces - 1) return;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            for (int q = 0; q < pieces; ++q) {
+                if (q == piece) continue;
+#pragma unroll
+                for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const f32x4_t v = *part_at(q, fm, fn, g);
+                            acc[fm][fn][4 * g] += v[0];
+                            acc[fm][fn][4 * g + 1] += v[1];
+                            acc[fm][fn][4 * g + 2] += v[2];
+                            acc[fm][fn][4 * g + 3] += v[3];
+                        }
+            }
+            if (tid == 0) p.counters[piece_tile] = 0;  // ready for the next launch
+        }
     }
 
     // ---- epilogue ----------------------------------------------------------------------------
@@ -600,6 +683,8 @@ static hipError_t launch_cfg(const GemmArgs& a, TileCfgId cfg, Epi epi, int64_t 
         case CFG_256x128: return launch_epi<Cfg256x128, GROUPED>(a, epi, tiles, stream);
         case CFG_128x128: return launch_epi<Cfg128x128, GROUPED>(a, epi, tiles, stream);
         case CFG_256x128_2WG: return launch_epi<Cfg256x128x2, GROUPED>(a, epi, tiles, stream);
+        case CFG_128x256: return launch_epi<Cfg128x256, GROUPED>(a, epi, tiles, stream);
+        case CFG_128x256_4W: return launch_epi<Cfg128x256w4, GROUPED>(a, epi, tiles, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -23,7 +23,9 @@ enum TileCfgId : int {
     CFG_256x128 = 1,  // 4 waves of 128x64, BK 64, 3 LDS stages (144 KB)
     CFG_128x128 = 2,  // 4 waves of 64x64, BK 64, 2 LDS stages (64 KB)
     CFG_256x128_2WG = 3,  // 4 waves of 128x64, BK 32, 3 LDS stages (72 KB), two workgroups per CU
-    CFG_COUNT = 4
+    CFG_128x256 = 4,  // 8 waves of 64x64, BK 64, 3 LDS stages (144 KB)
+    CFG_128x256_4W = 5,  // 4 waves of 128x64, BK 64, 3 LDS stages (144 KB)
+    CFG_COUNT = 6
 };
 
 struct GemmArgs {
@@ -45,6 +47,13 @@ struct GemmArgs {
     const uint16_t* B;
     int64_t ldb;
     int64_t b_stride;  // elements between consecutive experts' weight matrices
+    // grouped product: the last partial round of tiles is split along K into pieces that run
+    // concurrently; each piece stores its fp32 partial tile, and the last piece of a tile to
+    // finish (counted with an atomic) adds the others and writes the output.  split_slots is the
+    // number of workgroups the device runs at once (0: no splitting).
+    float* partials;      // [kSplitMaxPieces][BM * BN] fp32
+    int32_t* counters;    // [kSplitMaxPieces], zero at kernel start
+    int split_slots;
     // epilogue
     void* C;
     int64_t ldc;
@@ -53,6 +62,11 @@ struct GemmArgs {
     int num_shards;
     int64_t ldd;
 };
+
+// Split-K tail of the grouped product: at most this many pieces (and finished-piece counters) and
+// at most this many pieces per tile (the last piece reads the others' partial tiles).
+static constexpr int kSplitMaxPieces = 256;
+static constexpr int kSplitMaxPerTile = 8;
 
 struct TileShape {
     int bm, bn;
@@ -78,9 +92,11 @@ struct DispatchPlan {
     size_t ws_bytes;    // workspace needed
 };
 DispatchPlan plan_dispatch(int64_t T, int top_k, int num_local);
+// `zero` (n_zero int32, may be null) is cleared by the scan kernel: the grouped product's
+// finished-piece counters.
 hipError_t launch_dispatch(const DispatchPlan& plan, const int32_t* topk_ids, int num_experts,
                            int expert_begin, int num_local, int tile_m, int32_t* offsets,
                            int32_t* perm, int32_t* tile_offsets, int32_t* slice_counts,
-                           hipStream_t stream);
+                           int32_t* zero, int n_zero, hipStream_t stream);
 
 }  // namespace pk

@@ -135,8 +135,11 @@ pk_status pk_gemm_reduce(int64_t M, int64_t N, int64_t K,
  *   Y[j][c] = sum_k X[perm[j] / top_k][k] * W[e][k][c]
  * with X T x K (ldx), W num_local consecutive K x N row-major matrices, Y T*top_k x N (ldy, y_dtype;
  * rows past offsets[num_local] are left untouched).  `workspace` is device scratch of at least
- * pk_grouped_gemm_workspace_size(T, top_k, num_local) bytes, owned by the caller; its contents
- * need no initialisation and are meaningless afterwards.  1 <= num_local <= 1024, 1 <= top_k <= 64.
+ * pk_grouped_gemm_workspace_size(T, top_k, num_local) bytes (about 64 MiB: besides the dispatch
+ * tables it holds fp32 partial tiles for the last, partial round of output tiles, which is split
+ * along K so that it fills the device), owned by the caller; its contents need no initialisation
+ * and are meaningless afterwards.  Calls that share a workspace must not overlap.
+ * 1 <= num_local <= 1024, 1 <= top_k <= 64.
  */
 pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num_experts,
                           int expert_begin, int num_local,

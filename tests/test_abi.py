@@ -103,7 +103,7 @@ def test_grouped_validation(lib):
     args = lambda **kw: [kw.get("T", 16), kw.get("top_k", 2), FAKE, kw.get("E", 8),
                          kw.get("begin", 0), kw.get("nl", 4), FAKE, kw.get("ldx", 64),
                          kw.get("K", 64), FAKE, kw.get("N", 64), FAKE, FAKE, FAKE,
-                         kw.get("ldy", 64), kw.get("dt", 0), FAKE, kw.get("ws", 1 << 20), None]
+                         kw.get("ldy", 64), kw.get("dt", 0), FAKE, kw.get("ws", ws), None]
     assert lib.pk_grouped_gemm(*args(top_k=0)) == 1
     assert lib.pk_grouped_gemm(*args(nl=0)) == 1
     assert lib.pk_grouped_gemm(*args(begin=6)) == 1          # local range beyond num_experts
