@@ -205,7 +205,31 @@ def cpu_baseline(name, target_s):
     threads = oracle.default_threads()
     o = oracle.default()
     if w.kind == "grouped":
-        return None
+        # the oracle's dispatch, then its grouped product over the rows of the last experts
+        # (a suffix of the expert list, grown until it takes about target_s)
+        ids, X, W = pk_inputs.moe_inputs(w)
+        _, offsets, perm = o.dispatch(ids, w.num_experts, w.expert_begin, w.num_local)
+        total = int(offsets[-1])
+
+        def timed_g(e0):
+            sub_off = (offsets[e0:] - offsets[e0]).astype(np.int32)
+            sub_perm = perm[offsets[e0]:]
+            t = time.perf_counter()
+            o.grouped_gemm(sub_off, sub_perm, w.top_k, X, W[e0:], nthreads=threads)
+            return time.perf_counter() - t, int(sub_off[-1])
+
+        e0 = w.num_local - 1
+        dt, rows = timed_g(e0)
+        while e0 > 0 and dt < target_s:
+            per_row = dt / max(rows, 1)
+            want = target_s / per_row
+            while e0 > 0 and int(offsets[-1] - offsets[e0]) < want:
+                e0 -= 1
+            dt, rows = timed_g(e0)
+        flops = 2.0 * rows * w.N * w.K
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": "%d of %d dispatched rows (experts %d..%d of %d), K=%d, N=%d (%.1f s)"
+                          % (rows, total, e0, w.num_local - 1, w.num_local, w.K, w.N, dt)}
     A = pk_inputs.normal_bf16((w.M, w.K), w.std_a, w.seed_a)
     B = pk_inputs.normal_bf16((w.K, w.N), w.std_b, w.seed_b)
     D0 = np.zeros((1, w.N), np.float32)

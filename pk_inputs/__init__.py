@@ -22,15 +22,24 @@ __all__ = [
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """binary32 -> bf16 bit patterns, round to nearest even (input preparation only)."""
+    """binary32 -> bf16 bit patterns, round to nearest even (input preparation only).
+
+    Works in 32-bit unsigned arithmetic, in chunks: adding 0x7FFF plus the kept bit's parity can
+    only wrap around for NaN patterns, which are replaced by the quiet NaN 0x7FC0 anyway."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
-    nan = np.isnan(x)
-    if nan.any():
-        out[nan] = 0x7FC0
-    return out
+    flat = x.reshape(-1)
+    u = flat.view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    step = 1 << 24
+    for i in range(0, u.size, step):
+        v = u[i:i + step]
+        r = (v + np.uint32(0x7FFF) + ((v >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+        o = r.astype(np.uint16)
+        nan = np.isnan(flat[i:i + step])
+        if nan.any():
+            o[nan] = 0x7FC0
+        out[i:i + step] = o
+    return out.reshape(x.shape)
 
 
 def normal_bf16(shape, std: float, seed: int) -> np.ndarray:
