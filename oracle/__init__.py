@@ -97,6 +97,9 @@ class Oracle:
         lib.pk_oracle_dispatch.restype = i64
         lib.pk_oracle_grouped_gemm.argtypes = [i32, p, p, i32, p, i64, i64, p, i64, p, i64, i32]
         lib.pk_oracle_grouped_gemm.restype = i32
+        lib.pk_oracle_combine.argtypes = [i64, i32, i32, p, p, p, i64, i64, p, i64, p, p, i64, p,
+                                          i32]
+        lib.pk_oracle_combine.restype = i32
         self.lib = lib
         self.path = path
 
@@ -220,6 +223,36 @@ class Oracle:
         return Y
 
 
+    def combine(self, T: int, top_k: int, offsets, perm, H, W, gates, out0=None,
+                tokens=None, nthreads: int = 0) -> np.ndarray:
+        """out[t] = out0[t] + sum over dispatched rows j of token t of gates[perm[j]] * (H[j] . W[e])
+        (binary64, T x N).  With `tokens`, only those token rows are computed (the rest of the
+        result is out0, or zero)."""
+        H, W = _bf16(H), _bf16(W)
+        offsets = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
+        perm = np.ascontiguousarray(np.asarray(perm, dtype=np.int32))
+        gates = np.ascontiguousarray(np.asarray(gates, dtype=np.float32).reshape(-1))
+        num_local = offsets.shape[0] - 1
+        if W.ndim != 3 or W.shape[0] != num_local or H.shape[1] != W.shape[1]:
+            raise ValueError("combine shapes H %s W %s num_local %d" % (H.shape, W.shape, num_local))
+        if gates.shape[0] < T * top_k:
+            raise ValueError("gates must hold T * top_k values")
+        K, N = W.shape[1], W.shape[2]
+        out = np.zeros((T, N), dtype=np.float64) if out0 is None else \
+            np.ascontiguousarray(np.asarray(out0, dtype=np.float64)).copy()
+        mask = None
+        if tokens is not None:
+            mask = np.zeros(max(T, 1), dtype=np.uint8)
+            mask[np.asarray(tokens, dtype=np.int64)] = 1
+        rc = self.lib.pk_oracle_combine(T, top_k, num_local, _ptr(offsets), _ptr(perm), _ptr(H),
+                                        H.shape[1], K, _ptr(W), N, _ptr(gates), _ptr(out), N,
+                                        _ptr(mask) if mask is not None else None,
+                                        nthreads or default_threads())
+        if rc:
+            raise RuntimeError("pk_oracle_combine failed (%d)" % rc)
+        return out
+
+
 _default = None
 
 
@@ -263,6 +296,10 @@ def dispatch(topk_ids, num_experts: int, expert_begin: int, num_local: int):
 
 def grouped_gemm(offsets, perm, top_k: int, X, W, nthreads: int = 0):
     return default().grouped_gemm(offsets, perm, top_k, X, W, nthreads)
+
+
+def combine(T, top_k, offsets, perm, H, W, gates, out0=None, tokens=None, nthreads: int = 0):
+    return default().combine(T, top_k, offsets, perm, H, W, gates, out0, tokens, nthreads)
 
 
 def _load():

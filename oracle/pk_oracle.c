@@ -14,7 +14,9 @@
  *     atomically added at the destination", i.e. D_final = D_initial + sum over producers of A_p B_p
  *     (a sum; no order is specified);
  *   - token dispatch + expert GEMM: routed tokens are grouped per expert and multiplied by that
- *     expert's weight matrix.
+ *     expert's weight matrix;
+ *   - combine (the other side of dispatch): each dispatched row's expert output is weighted by
+ *     its routing gate and added back into its token's output row.
  *
  * Arithmetic: every product and sum is taken in IEEE binary64 over the bf16 inputs decoded
  * exactly; sums run in ascending index order.  bf16 outputs are the binary64 result rounded once,
@@ -249,6 +251,53 @@ int pk_oracle_grouped_gemm(int num_local, const int32_t* offsets, const int32_t*
         int rc = run_gemm(rows, N, K, Ag, K, W + (int64_t)e * K * N, N, Y + r0 * ldy, ldy, 0,
                           nthreads);
         free(Ag);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* Combine after the down projection: for every dispatched row j of local expert e (offsets[e] <=
+   j < offsets[e+1]), with routing slot f = perm[j] and token t = f / top_k,
+       out[t, :] += gates[f] * (H[j, :] . W_e)
+   H is rows x K bf16 in dispatched order (leading dimension ldh); W is num_local consecutive K x N
+   bf16 matrices; gates is binary32 per routing slot; out is T x N binary64 (leading dimension
+   ldo), accumulated into.  If token_mask is not NULL only tokens t with token_mask[t] != 0 are
+   computed (their rows; other rows are skipped).  Each expert output row is a plain product in
+   ascending k; the weighted rows are then added in ascending j. */
+int pk_oracle_combine(int64_t T, int top_k, int num_local, const int32_t* offsets,
+                      const int32_t* perm, const uint16_t* H, int64_t ldh, int64_t K,
+                      const uint16_t* W, int64_t N, const float* gates, double* out, int64_t ldo,
+                      const uint8_t* token_mask, int nthreads) {
+    if (T < 0 || top_k <= 0 || num_local < 0 || K < 0 || N < 0) return 1;
+    for (int e = 0; e < num_local; ++e) {
+        const int64_t r0 = offsets[e], r1 = offsets[e + 1];
+        if (r1 <= r0 || N == 0) continue;
+        /* rows of this expert that belong to selected tokens */
+        int64_t* sel = (int64_t*)malloc(sizeof(int64_t) * (size_t)(r1 - r0));
+        if (!sel) return 2;
+        int64_t n = 0;
+        for (int64_t j = r0; j < r1; ++j) {
+            const int64_t f = perm[j], t = f / top_k;
+            if (f < 0 || t >= T) { free(sel); return 3; }
+            if (!token_mask || token_mask[t]) sel[n++] = j;
+        }
+        if (n == 0) { free(sel); continue; }
+        uint16_t* Hs = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(n * (K > 0 ? K : 1)));
+        double* Z = (double*)malloc(sizeof(double) * (size_t)(n * N));
+        if (!Hs || !Z) { free(sel); free(Hs); free(Z); return 2; }
+        for (int64_t i = 0; i < n; ++i)
+            memcpy(Hs + i * K, H + sel[i] * ldh, sizeof(uint16_t) * (size_t)K);
+        int rc = run_gemm(n, N, K, Hs, K, W + (int64_t)e * K * N, N, Z, N, 0, nthreads);
+        if (!rc) {
+            for (int64_t i = 0; i < n; ++i) {
+                const int64_t f = perm[sel[i]], t = f / top_k;
+                const double g = (double)gates[f];
+                double* o = out + t * ldo;
+                const double* z = Z + i * N;
+                for (int64_t c = 0; c < N; ++c) o[c] += g * z[c];
+            }
+        }
+        free(sel); free(Hs); free(Z);
         if (rc) return rc;
     }
     return 0;

@@ -379,4 +379,99 @@ def pin_grouped_brute_force(o):
 GROUPED_PINS = [pin_grouped_selection_weights, pin_grouped_one_expert_is_gemm,
                 pin_grouped_brute_force]
 
-ALL_PINS = BF16_PINS + GEMM_PINS + REDUCE_PINS + DISPATCH_PINS + GROUPED_PINS
+def _dispatched_row(ids, begin, nl):
+    """Row index of every local routing slot in the stable expert-major order, counted directly
+    from the routing table (independent of the oracle's dispatch): slots of lower experts first,
+    then earlier slots of the same expert."""
+    flat = np.asarray(ids).reshape(-1)
+    local = (flat >= begin) & (flat < begin + nl)
+    row = {}
+    for f in range(flat.size):
+        if not local[f]:
+            continue
+        e = flat[f] - begin
+        lower = int(np.sum(local & (flat - begin < e)))
+        earlier = int(np.sum(local[:f] & (flat[:f] == flat[f])))
+        row[f] = lower + earlier
+    return row
+
+
+def pin_combine_selection_weights(o):
+    """Combine with selection weights: W_e[k, n] = 2^(e mod 8 - 4) if k == n + c_e, H[j, k] =
+    (j + 1) * 2^(k mod 8 - 4), gates 2^-(f mod 4).  Every term and every sum is exact, so
+    out[t, n] = sum over the local slots f of t of gate_f * 2^(e mod 8 - 4) * H[row(f), n + c_e]
+    exactly, with row(f) counted from the routing table.  Pins the token each row goes back to, the
+    gate it is weighted by, the expert weight and the destination term."""
+    T, top_k, E, begin, nl, K, N = 30, 3, 10, 2, 5, 48, 12
+    ids = pk_inputs.zipf_topk(T, E, top_k, 0.3, 131)
+    c, off, perm = o.dispatch(ids, E, begin, nl)
+    rows = int(off[-1])
+    jj = np.arange(rows)[:, None].astype(np.float64)
+    kk = np.arange(K)[None, :].astype(np.float64)
+    Hv = (jj + 1.0) * 2.0 ** (kk % 8 - 4)
+    H = _bits(Hv)
+    assert np.array_equal(bf16_bits_to_f64(H), Hv)
+    W = np.zeros((nl, K, N), dtype=np.float64)
+    shift = [(5 * e) % (K - N + 1) for e in range(nl)]
+    for e in range(nl):
+        for n in range(N):
+            W[e, n + shift[e], n] = 2.0 ** (e % 8 - 4)
+    gates = (2.0 ** -(np.arange(T * top_k) % 4)).astype(np.float32)
+    out0 = np.arange(T * N, dtype=np.float64).reshape(T, N) * 0.25
+    got = o.combine(T, top_k, off, perm, H, _bits(W), gates, out0=out0)
+    want = out0.copy()
+    row = _dispatched_row(ids, begin, nl)
+    flat = ids.reshape(-1)
+    for f, j in row.items():
+        e = flat[f] - begin
+        want[f // top_k] += float(gates[f]) * 2.0 ** (e % 8 - 4) * Hv[j, shift[e]:shift[e] + N]
+    assert np.array_equal(got, want)
+
+
+def pin_combine_brute_force(o):
+    """Tiny combine against exact rationals, slot by slot from the routing table."""
+    T, top_k, E, begin, nl, K, N = 5, 2, 4, 1, 3, 4, 3
+    ids = np.array([[1, 3], [2, 1], [0, 3], [3, 2], [1, 0]], dtype=np.int32)
+    c, off, perm = o.dispatch(ids, E, begin, nl)
+    rows = int(off[-1])
+    H = pk_inputs.normal_bf16((rows, K), 1.0, 141)
+    W = pk_inputs.normal_bf16((nl, K, N), 1.0, 142)
+    gates = np.random.Generator(np.random.PCG64(143)).random(T * top_k).astype(np.float32)
+    h, w = bf16_bits_to_f64(H), bf16_bits_to_f64(W)
+    got = o.combine(T, top_k, off, perm, H, W, gates)
+    row = _dispatched_row(ids, begin, nl)
+    flat = ids.reshape(-1)
+    for t in range(T):
+        for n in range(N):
+            exact, bound = Fraction(0), Fraction(0)
+            for k in range(top_k):
+                f = t * top_k + k
+                if f not in row:
+                    continue
+                e, j = flat[f] - begin, row[f]
+                g = Fraction(float(gates[f]))
+                exact += g * sum(Fraction(h[j, q]) * Fraction(w[e, q, n]) for q in range(K))
+                bound += abs(g) * sum(abs(Fraction(h[j, q]) * Fraction(w[e, q, n])) for q in range(K))
+            assert abs(Fraction(got[t, n]) - exact) <= bound * Fraction(2 * (K + top_k) * 2.0 ** -53)
+
+
+def pin_combine_token_subset(o):
+    """Computing only some tokens gives exactly those rows of the full result (the rest is the
+    initial value)."""
+    T, top_k, E, nl, K, N = 24, 4, 8, 8, 32, 16
+    ids = pk_inputs.zipf_topk(T, E, top_k, 1.0, 151)
+    c, off, perm = o.dispatch(ids, E, 0, nl)
+    H = pk_inputs.normal_bf16((int(off[-1]), K), 1.0, 152)
+    W = pk_inputs.normal_bf16((nl, K, N), 0.1, 153)
+    gates = np.random.Generator(np.random.PCG64(154)).random(T * top_k).astype(np.float32)
+    full = o.combine(T, top_k, off, perm, H, W, gates)
+    sub = [1, 7, 19]
+    part = o.combine(T, top_k, off, perm, H, W, gates, tokens=sub)
+    assert np.array_equal(part[sub], full[sub])
+    others = [t for t in range(T) if t not in sub]
+    assert np.all(part[others] == 0.0)
+
+
+COMBINE_PINS = [pin_combine_selection_weights, pin_combine_brute_force, pin_combine_token_subset]
+
+ALL_PINS = BF16_PINS + GEMM_PINS + REDUCE_PINS + DISPATCH_PINS + GROUPED_PINS + COMBINE_PINS

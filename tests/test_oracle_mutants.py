@@ -1,7 +1,8 @@
 """The pins are sensitive: a copy of the oracle with one plausible mistake planted in its C source
 (compiled here, on the CPU) must fail at least one pin.  Mistakes cover a dropped term, a sign, an
 index/transposition, the rounding rule, dispatch stability and range checks, the gathered row,
-the expert weight choice and the destination term of the reduction."""
+the expert weight choice, the destination term of the reduction, and the gate, token and
+accumulation of the combine."""
 import os
 
 import pytest
@@ -34,6 +35,14 @@ MUTANTS = [
      "R[i * ldr + j] = 0.0;", _pins.REDUCE_PINS),
     ("drop_last_producer", "for (int p = 0; p < num_producers; ++p) {",
      "for (int p = 0; p < num_producers - 1; ++p) {", _pins.REDUCE_PINS),
+    ("combine_drop_gate", "for (int64_t c = 0; c < N; ++c) o[c] += g * z[c];",
+     "for (int64_t c = 0; c < N; ++c) o[c] += z[c];", _pins.COMBINE_PINS),
+    ("combine_wrong_token", "double* o = out + t * ldo;", "double* o = out + (f % T) * ldo;",
+     _pins.COMBINE_PINS),
+    ("combine_gate_of_row", "const double g = (double)gates[f];",
+     "const double g = (double)gates[sel[i]];", _pins.COMBINE_PINS),
+    ("combine_overwrite", "for (int64_t c = 0; c < N; ++c) o[c] += g * z[c];",
+     "for (int64_t c = 0; c < N; ++c) o[c] = g * z[c];", _pins.COMBINE_PINS),
 ]
 
 
