@@ -60,6 +60,11 @@ def library() -> ctypes.CDLL:
     lib.pk_grouped_gemm.restype = i32
     lib.pk_grouped_gemm_workspace_size.argtypes = [i64, i32, i32]
     lib.pk_grouped_gemm_workspace_size.restype = sz
+    lib.pk_grouped_combine.argtypes = [i64, i32, i32, p, p, p, i64, i64, p, i64, p, p, i64, p, sz,
+                                       p]
+    lib.pk_grouped_combine.restype = i32
+    lib.pk_grouped_combine_workspace_size.argtypes = [i32]
+    lib.pk_grouped_combine_workspace_size.restype = sz
     lib.pk_status_string.argtypes = [i32]
     lib.pk_status_string.restype = ctypes.c_char_p
     lib.pk_last_error.argtypes = []
@@ -158,6 +163,42 @@ def gemm_reduce(A: torch.Tensor, B: torch.Tensor, D: Union[torch.Tensor, Sequenc
                                     shards[0].size(0), lds.pop(), mode, op, ldo,
                                     _stream_handle(stream)))
     return D
+
+
+def grouped_combine_workspace_size(num_local: int) -> int:
+    return int(library().pk_grouped_combine_workspace_size(num_local))
+
+
+def grouped_combine(T: int, top_k: int, offsets: torch.Tensor, perm: torch.Tensor,
+                    H: torch.Tensor, W: torch.Tensor, gates: torch.Tensor, out: torch.Tensor,
+                    workspace: torch.Tensor, stream=None):
+    """Combine after the expert down-projection (pk_grouped_combine): out[t] += sum over the
+    dispatched rows j of token t of gates[perm[j]] * (H[j] . W[e(j)]).  ``offsets``/``perm`` come
+    from :func:`grouped_gemm`; ``H`` is (>= rows) x K bf16 in dispatched order, ``W`` num_local x
+    K x N, ``gates`` T*top_k fp32 (slot order), ``out`` T x N fp32 (accumulated into)."""
+    hp, ldh = _matrix(H, _BF16_LIKE, "H")
+    if W.dim() != 3 or not W.is_contiguous() or W.dtype not in _BF16_LIKE or not W.is_cuda:
+        raise TypeError("W must be a contiguous num_local x K x N bf16 device tensor")
+    num_local, K, N = W.shape
+    if H.size(1) != K:
+        raise ValueError("H has %d columns, W expects K=%d" % (H.size(1), K))
+    for t, n, what in ((offsets, num_local + 1, "offsets"), (perm, T * top_k, "perm")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() < n:
+            raise TypeError("%s must be a contiguous int32 device tensor of >= %d entries" % (what, n))
+    if gates.dtype != torch.float32 or not gates.is_cuda or not gates.is_contiguous() \
+            or gates.numel() < T * top_k:
+        raise TypeError("gates must be a contiguous fp32 device tensor of >= %d entries" % (T * top_k))
+    op, ldo = _matrix(out, (torch.float32,), "out")
+    if out.size(0) != T or out.size(1) != N:
+        raise ValueError("out must be %d x %d" % (T, N))
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous device tensor")
+    _check(library().pk_grouped_combine(T, top_k, num_local, offsets.data_ptr(), perm.data_ptr(),
+                                        hp, ldh, K, W.data_ptr(), N, gates.data_ptr(), op, ldo,
+                                        workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream)))
+    return out
 
 
 def grouped_gemm_workspace_size(T: int, top_k: int, num_local: int) -> int:

@@ -286,4 +286,65 @@ pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num
     return hip_status(pk::launch_grouped(a, cfg, epi, max_tiles, s), "pk_grouped_gemm launch");
 }
 
+size_t pk_grouped_combine_workspace_size(int num_local) {
+    if (num_local < 1 || num_local > 1024) return 0;
+    return align256(sizeof(int32_t) * (size_t)(num_local + 1));
+}
+
+pk_status pk_grouped_combine(int64_t T, int top_k, int num_local, const int32_t* offsets,
+                             const int32_t* perm, const uint16_t* H, int64_t ldh, int64_t K,
+                             const uint16_t* W, int64_t N, const float* gates, float* out,
+                             int64_t ldo, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (T < 0 || K < 0 || N < 0) return fail(PK_ERR_INVALID_ARGUMENT, "negative size");
+    if (top_k < 1 || top_k > 64) return fail(PK_ERR_INVALID_ARGUMENT, "top_k outside 1..64");
+    if (num_local < 1 || num_local > 1024) return fail(PK_ERR_INVALID_ARGUMENT, "num_local outside 1..1024");
+    if (T == 0 || N == 0) return ok();
+    if (T * (int64_t)top_k > INT32_MAX) return fail(PK_ERR_UNSUPPORTED, "more than 2^31 routing slots");
+    if (!offsets || !perm || !gates || !out || !workspace || (K > 0 && (!H || !W)))
+        return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
+    if ((K > 0 && ldh < K) || ldo < N) return fail(PK_ERR_INVALID_ARGUMENT, "leading dimension too small");
+    const size_t need = pk_grouped_combine_workspace_size(num_local);
+    if (workspace_bytes < need)
+        return fail(PK_ERR_INVALID_ARGUMENT, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (K % 8 || N % 8) return fail(PK_ERR_UNSUPPORTED, "K and N must be multiples of 8");
+    if ((K > 0 && ldh % 8) || ldo % 4)
+        return fail(PK_ERR_UNSUPPORTED, "leading dimensions must be 16-byte multiples");
+    if ((K > 0 && (!aligned16(H) || !aligned16(W))) || !aligned16(out) || !aligned16(workspace))
+        return fail(PK_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+    if (K == 0) return ok();  // nothing to add
+
+    hipStream_t s = (hipStream_t)stream;
+    const pk::TileCfgId cfg = kGroupedCfg;
+    const pk::TileShape t = pk::tile_shape(cfg);
+    int32_t* tile_offsets = (int32_t*)workspace;
+    hipError_t e = pk::launch_tile_prefix(offsets, num_local, t.bm, tile_offsets, s);
+    if (e != hipSuccess) return hip_status(e, "pk_grouped_combine tile list launch");
+
+    pk::GemmArgs a{};
+    a.M = T * (int64_t)top_k;
+    a.N = N; a.K = K;
+    a.a_ptr[0] = H;
+    a.num_chunks = 1;
+    a.chunk_rows = a.M;
+    a.lda = ldh;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.tile_offsets = tile_offsets;
+    a.top_k = top_k;
+    a.num_local = num_local;
+    a.B = W; a.ldb = N;
+    a.b_stride = K * N;
+    a.gates = gates;
+    a.C = out; a.ldc = ldo;
+    int slots = device_cu_count();
+    if (slots > pk::kSplitMaxPieces) slots = pk::kSplitMaxPieces;
+    a.split_slots = slots > 0 ? slots : 0;  // pieces add their own weighted partials
+    const int64_t rows_max = T * (int64_t)top_k;
+    const int64_t max_tiles = (rows_max / t.bm + num_local) * ceil_div(N, t.bn) + 8 +
+                              pk::kSplitMaxPieces;
+    return hip_status(pk::launch_grouped(a, cfg, pk::EPI_COMBINE, max_tiles, s),
+                      "pk_grouped_combine launch");
+}
+
 }  // extern "C"

@@ -160,6 +160,32 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* ids
     }
 }
 
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* offsets, int num_local,
+                                                           int tile_m, int32_t* tile_offsets) {
+    __shared__ int scan[kMaxLocal];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < num_local; e += blockDim.x)
+        scan[e] = (offsets[e + 1] - offsets[e] + tile_m - 1) / tile_m;
+    __syncthreads();
+    for (int d = 1; d < num_local; d <<= 1) {
+        int v = 0;
+        const bool act = tid < num_local && tid >= d;
+        if (act) v = scan[tid - d];
+        __syncthreads();
+        if (act) scan[tid] += v;
+        __syncthreads();
+    }
+    if (tid == 0) tile_offsets[0] = 0;
+    for (int e = tid; e < num_local; e += blockDim.x) tile_offsets[e + 1] = scan[e];
+}
+
+hipError_t launch_tile_prefix(const int32_t* offsets, int num_local, int tile_m,
+                              int32_t* tile_offsets, hipStream_t stream) {
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, stream, offsets, num_local,
+                       tile_m, tile_offsets);
+    return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const DispatchPlan& plan, const int32_t* topk_ids, int num_experts,
                            int expert_begin, int num_local, int tile_m, int32_t* offsets,
                            int32_t* perm, int32_t* tile_offsets, int32_t* slice_counts,

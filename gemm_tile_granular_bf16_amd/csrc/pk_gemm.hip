@@ -246,10 +246,10 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
         int64_t r = row0 + rl;
         if (r >= row_end) r = row0;  // masked row: read a valid one, never stored
         const uint16_t* src;
-        if constexpr (GROUPED) {
+        if constexpr (GROUPED && EPI != EPI_COMBINE) {
             const int64_t token = p.perm[r] / p.top_k;
             src = p.a_ptr[0] + token * p.lda;
-        } else if (p.num_chunks == 1) {
+        } else if (GROUPED || p.num_chunks == 1) {
             src = p.a_ptr[0] + r * p.lda;
         } else {
             const int ch = (int)(r / p.chunk_rows);
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
         }
     };
     // Transposed blocks (row-contiguous lanes) for every epilogue except the atomic one.
-    constexpr bool ROWS_IN_LANES = EPI != EPI_ATOMIC_F32;
+    constexpr bool ROWS_IN_LANES = EPI != EPI_ATOMIC_F32 && EPI != EPI_COMBINE;
     auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
         step(j, std::integral_constant<int, MODE_LAST>{});
     }
 
-    if constexpr (GROUPED) {
+    if constexpr (GROUPED && (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32)) {
         if (piece >= 0) {
             // One piece of a split tile: store the fp32 partial tile (this layout, 16-byte
             // vectors), publish it, and count the piece.  The piece that completes the count adds
@@ -613,6 +613,47 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
                 });
             }
         }
+    } else if constexpr (EPI == EPI_COMBINE) {
+        // Combine: every row j of the tile goes back to its token t = perm[j] / top_k, weighted by
+        // the gate of its routing slot, with fp32 atomics (several experts of one token, and other
+        // producers, add into the same output row).  The tile's row -> (token, gate) table is
+        // staged in LDS once; in the natural orientation 32 lanes then cover 128 contiguous bytes
+        // of one output row per atomic instruction.
+        __shared__ int tok_of[C::BM];
+        __shared__ float gate_of[C::BM];
+        for (int i = tid; i < C::BM; i += C::NT) {
+            const int64_t j = row0 + i;
+            int tk = -1;
+            float g = 0.0f;
+            if (j < row_end) {
+                const int32_t f = p.perm[j];
+                tk = f / p.top_k;
+                g = p.gates[f];
+            }
+            tok_of[i] = tk;
+            gate_of[i] = g;
+        }
+        __syncthreads();
+        float* const out = (float*)p.C;
+        const int lrow = (lane >> 5) * 4;
+        const int lcol = lane & 31;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wy * C::WTM + fm * 32 + (r >> 2) * 8 + lrow + (r & 3);
+                const int tk = tok_of[row];
+                const float g = gate_of[row];
+                if (tk < 0) continue;
+                float* const orow = out + (int64_t)tk * p.ldc;
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn) {
+                    const int64_t col = wcol0 + fn * 32 + lcol;
+                    if (col < N)
+                        __hip_atomic_fetch_add(orow + col, g * acc[fm][fn][r], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
     } else {
         // Reduction into the destination with fp32 atomics (natural orientation: register r of
         // block (fm, fn) in lane l is row fm*32 + (r/4)*8 + (l/32)*4 + r%4, column fn*32 + l%32,
@@ -670,6 +711,9 @@ static hipError_t launch_epi(const GemmArgs& a, Epi epi, int64_t tiles, hipStrea
             break;
         case EPI_OWNER_CAST:
             if constexpr (!GROUPED) return launch_one<C, false, EPI_OWNER_CAST>(a, tiles, stream);
+            break;
+        case EPI_COMBINE:
+            if constexpr (GROUPED) return launch_one<C, true, EPI_COMBINE>(a, tiles, stream);
             break;
     }
     return hipErrorInvalidValue;

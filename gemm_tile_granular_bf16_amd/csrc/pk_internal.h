@@ -14,7 +14,9 @@ enum Epi : int {
     EPI_STORE_F32 = 1,   // C = acc
     EPI_ATOMIC_F32 = 2,  // D += acc, one fp32 atomic add per element
     EPI_OWNER_F32 = 3,   // D += acc, owner-exclusive vector read-modify-write
-    EPI_OWNER_CAST = 4   // as EPI_OWNER_F32, and C = bf16(D + acc) (round to nearest even)
+    EPI_OWNER_CAST = 4,  // as EPI_OWNER_F32, and C = bf16(D + acc) (round to nearest even)
+    EPI_COMBINE = 5      // grouped only: out[token(j)] += gate(j) * acc, fp32 atomics; A rows are
+                         // read directly (already in dispatched order), not gathered
 };
 
 // Tile shapes compiled into the library (see pk_gemm.hip for what each is used for).
@@ -54,6 +56,7 @@ struct GemmArgs {
     float* partials;      // [kSplitMaxPieces][BM * BN] fp32
     int32_t* counters;    // [kSplitMaxPieces], zero at kernel start
     int split_slots;
+    const float* gates;   // EPI_COMBINE: gate per routing slot
     // epilogue
     void* C;
     int64_t ldc;
@@ -83,6 +86,11 @@ hipError_t launch_grouped(const GemmArgs& a, TileCfgId cfg, Epi epi, int64_t max
 // fp32 destination rows [0, M) -> bf16 (round to nearest even), shard by shard.
 hipError_t launch_cast(float* const* d_ptr, int num_shards, int64_t shard_rows, int64_t ldd,
                        int64_t M, int64_t N, uint16_t* out, int64_t ldo, hipStream_t stream);
+
+// Per-expert M-tile prefix (tile_offsets[e] = sum_{e' < e} ceil(count_e' / tile_m)) from the
+// dispatch offsets, on the device (one workgroup, num_local <= 1024).
+hipError_t launch_tile_prefix(const int32_t* offsets, int num_local, int tile_m,
+                              int32_t* tile_offsets, hipStream_t stream);
 
 // Dispatch: counts, offsets, stable permutation and per-expert M-tile prefix.
 struct DispatchPlan {

@@ -12,7 +12,9 @@
  *   pk_gemm_reduce   -- local product whose output tiles are added into destination shards, with
  *                       an optional bf16 cast pass (receiving side of GEMM+RS / GEMM+AR);
  *   pk_grouped_gemm  -- token dispatch (stable grouping of routed slots per local expert) followed
- *                       by the per-expert product over the gathered rows.
+ *                       by the per-expert product over the gathered rows;
+ *   pk_grouped_combine -- the per-expert down-projection of the dispatched rows, weighted by the
+ *                       routing gates and added back into token order.
  *
  * Conventions shared by every entry point:
  *   - bf16 values are passed as uint16_t bit patterns (IEEE binary32 upper halves).
@@ -152,6 +154,36 @@ pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num
 
 /* Device workspace bytes pk_grouped_gemm needs for this routing shape (0 on invalid sizes). */
 size_t pk_grouped_gemm_workspace_size(int64_t T, int top_k, int num_local);
+
+/*
+ * pk_grouped_combine -- the other side of token dispatch: the expert down-projection of the
+ * dispatched rows, weighted by each row's routing gate and added back into its token's output
+ * row ("Loads and Loads of Fluffy Kittens" summary, Key claims and Results: expert parallelism,
+ * D_expert = 2048 -> D = 7168; the expert outputs return to their tokens and are summed).
+ *
+ *   out[t][c] += sum over dispatched rows j with perm[j] / top_k == t of
+ *                gates[perm[j]] * sum_k H[j][k] * W[e(j)][k][c]
+ *
+ * offsets[num_local + 1] and perm are the device outputs of pk_grouped_gemm for the same routing
+ * (row j belongs to local expert e when offsets[e] <= j < offsets[e+1]).  H is the dispatched-row
+ * input, rows in that same order, T*top_k x K capacity (ldh); W is num_local consecutive K x N
+ * row-major matrices; gates holds one fp32 weight per routing slot f = t*top_k + k; out is T x N
+ * fp32 (ldo), accumulated into with fp32 atomic adds, so other producers (other experts, other
+ * ranks) may add into it concurrently.  `workspace` is device scratch of at least
+ * pk_grouped_combine_workspace_size(num_local) bytes (the per-expert tile list).
+ * 1 <= num_local <= 1024, 1 <= top_k <= 64; K % 8 == 0, N % 8 == 0.
+ */
+pk_status pk_grouped_combine(int64_t T, int top_k, int num_local,
+                             const int32_t* offsets, const int32_t* perm,
+                             const uint16_t* H, int64_t ldh, int64_t K,
+                             const uint16_t* W, int64_t N,
+                             const float* gates,
+                             float* out, int64_t ldo,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Device workspace bytes pk_grouped_combine needs (0 on invalid sizes). */
+size_t pk_grouped_combine_workspace_size(int num_local);
 
 /* Static description of a status code. */
 const char* pk_status_string(pk_status s);

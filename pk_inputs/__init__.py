@@ -91,7 +91,7 @@ def rs_prefill(M: int, N: int, partials: int, std: float, seed0: int,
 class Workload:
     """One synthetic workload: its kind, sizes and seeds (values only; no arithmetic)."""
     name: str
-    kind: str                  # "reduce" | "gemm" | "grouped"
+    kind: str                  # "reduce" | "gemm" | "grouped" | "combine"
     M: int = 0
     N: int = 0
     K: int = 0
@@ -113,10 +113,11 @@ class Workload:
     expert_begin: int = 0
     zipf_s: float = 0.0
     seed_route: int = 0
+    seed_gates: int = 0        # combine: routing gate weights
 
     @property
     def flops(self) -> float:
-        if self.kind == "grouped":
+        if self.kind in ("grouped", "combine"):
             raise ValueError("grouped flops depend on the routed row count")
         return 2.0 * self.M * self.N * self.K * self.producers
 
@@ -133,6 +134,10 @@ WORKLOADS: Dict[str, Workload] = {
                         prefill_std=0.02 * 0.02 * 32.0, prefill_seed=4011),
     "ar_16384": Workload("ar_16384", "reduce", M=16384, N=16384, K=2048, seed_a=5001,
                          seed_b=5002, producers=1, shards=1, cast_bf16=True),
+    "moe_combine": Workload("moe_combine", "combine", K=2048, N=7168, std_a=1.0, std_b=0.02,
+                            seed_a=7001, seed_b=7002, tokens=4096, top_k=8, num_experts=256,
+                            num_local=32, expert_begin=0, zipf_s=1.1, seed_route=6003,
+                            seed_gates=7004),
     "moe_dispatch": Workload("moe_dispatch", "grouped", K=7168, N=2048, std_a=1.0, std_b=0.02,
                              seed_a=6001, seed_b=6002, tokens=4096, top_k=8, num_experts=256,
                              num_local=32, expert_begin=0, zipf_s=1.1, seed_route=6003),
@@ -152,6 +157,25 @@ def moe_inputs(w: Workload):
     X = normal_bf16((w.tokens, w.K), w.std_a, w.seed_a)
     W = normal_bf16((w.num_local, w.K, w.N), w.std_b, w.seed_b)
     return ids, X, W
+
+
+def topk_gates(T: int, top_k: int, seed: int) -> np.ndarray:
+    """Positive routing gate weights, T*top_k binary32 in slot order, each token's top_k weights
+    summing to one (uniform draws divided by their token's sum)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    g = rng.random((T, top_k), dtype=np.float32) + np.float32(0.05)
+    g /= g.sum(axis=1, keepdims=True)
+    return np.ascontiguousarray(g.reshape(-1).astype(np.float32))
+
+
+def combine_inputs(w: Workload):
+    """Routing and operands of the MoE combine workload: (topk_ids, H, W, gates).  H has one row
+    per routing slot (the capacity of the dispatched order); only the dispatched rows are read."""
+    ids = zipf_topk(w.tokens, w.num_experts, w.top_k, w.zipf_s, w.seed_route)
+    H = normal_bf16((w.tokens * w.top_k, w.K), w.std_a, w.seed_a)
+    W = normal_bf16((w.num_local, w.K, w.N), w.std_b, w.seed_b)
+    gates = topk_gates(w.tokens, w.top_k, w.seed_gates)
+    return ids, H, W, gates
 
 
 def describe() -> List[str]:

@@ -26,9 +26,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(pk_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pk_gemm", "pk_gemm_reduce", "pk_grouped_gemm", "pk_grouped_gemm_workspace_size",
+              "pk_grouped_combine", "pk_grouped_combine_workspace_size",
               "pk_status_string", "pk_last_error"):
         assert n in names
 
@@ -119,3 +120,20 @@ def test_python_binding_refuses_host_tensors(lib):
     a = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         pk.gemm(a, torch.zeros(8, 8, dtype=torch.bfloat16), torch.zeros(4, 8))
+
+
+def test_combine_validation(lib):
+    ws = lib.pk_grouped_combine_workspace_size(32)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.pk_grouped_combine_workspace_size(0) == 0
+    assert lib.pk_grouped_combine_workspace_size(2000) == 0
+    args = lambda **kw: [kw.get("T", 16), kw.get("top_k", 2), kw.get("nl", 4), FAKE, FAKE, FAKE,
+                         kw.get("ldh", 64), kw.get("K", 64), FAKE, kw.get("N", 64), FAKE, FAKE,
+                         kw.get("ldo", 64), FAKE, kw.get("ws", ws), None]
+    assert lib.pk_grouped_combine(*args(top_k=0)) == 1
+    assert lib.pk_grouped_combine(*args(nl=0)) == 1
+    assert lib.pk_grouped_combine(*args(T=-1)) == 1
+    assert lib.pk_grouped_combine(*args(ws=16)) == 1          # workspace too small
+    assert lib.pk_grouped_combine(*args(ldh=32)) == 1         # ldh < K
+    assert lib.pk_grouped_combine(*args(K=60, ldh=64)) == 2   # K % 8
+    assert lib.pk_grouped_combine(*args(ldo=66)) == 2         # ldo % 4

@@ -1,0 +1,145 @@
+"""pk_grouped_combine (gate-weighted scatter of the expert down-projection back to token order)
+against the oracle on the GPU, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import pk_inputs
+from _gpu import dev_bf16, host_f32, log, require_gpu
+from _parity import bf16_bits_to_f64, check_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pk():
+    return require_gpu()
+
+
+def _device_routing(o, ids, E, begin, nl):
+    """The oracle's dispatch tables (offsets, perm) as device inputs of the combine."""
+    _, off, perm = o.dispatch(ids, E, begin, nl)
+    T, top_k = ids.shape
+    perm_full = np.zeros(max(T * top_k, 1), dtype=np.int32)
+    perm_full[:perm.size] = perm
+    return off, perm, torch.from_numpy(off).cuda(), torch.from_numpy(perm_full).cuda()
+
+
+def _absbound(T, top_k, off, perm, H, W, gates, tokens):
+    """Per output element: sum over the token's rows of |gate| * sum_k |H||W| (numpy, binary64)."""
+    h, N = bf16_bits_to_f64(H), W.shape[2]
+    bound = np.zeros((len(tokens), N))
+    pos = {t: i for i, t in enumerate(tokens)}
+    for e in range(W.shape[0]):
+        we = np.abs(bf16_bits_to_f64(W[e]))
+        for j in range(off[e], off[e + 1]):
+            t = perm[j] // top_k
+            if t in pos:
+                bound[pos[t]] += abs(float(gates[perm[j]])) * (np.abs(h[j]) @ we)
+    return bound
+
+
+def _run(pk, T, top_k, nl, off_d, perm_d, H, W, gates, out0, stream=None):
+    out = torch.from_numpy(np.ascontiguousarray(out0, dtype=np.float32)).cuda()
+    ws = torch.empty(pk.grouped_combine_workspace_size(nl), dtype=torch.uint8, device="cuda")
+    pk.grouped_combine(T, top_k, off_d, perm_d, dev_bf16(H), dev_bf16(W),
+                       torch.from_numpy(gates).cuda(), out, ws, stream=stream)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("shape", [(300, 4, 16, 3, 6, 136, 264), (64, 2, 8, 0, 8, 512, 128),
+                                   (1000, 8, 64, 8, 16, 256, 520)],
+                         ids=["ragged", "small", "wide"])
+def test_combine_parity(pk, oracle_mod, shape):
+    """Random routing, gates, activations and weights; ragged K and N; a non-zero initial output.
+    Every output element against the oracle."""
+    T, top_k, E, begin, nl, K, N = shape
+    o = oracle_mod.default()
+    ids = pk_inputs.zipf_topk(T, E, top_k, 0.8, 161 + K)
+    off, perm, off_d, perm_d = _device_routing(o, ids, E, begin, nl)
+    H = pk_inputs.normal_bf16((T * top_k, K), 1.0, 162)
+    W = pk_inputs.normal_bf16((nl, K, N), 0.05, 163)
+    gates = pk_inputs.topk_gates(T, top_k, 164)
+    out0 = np.random.Generator(np.random.PCG64(165)).standard_normal((T, N)).astype(np.float32)
+    log("combine %s: running" % (shape,))
+    got = host_f32(_run(pk, T, top_k, nl, off_d, perm_d, H, W, gates, out0))
+    R = o.combine(T, top_k, off, perm, H, W, gates, out0=out0)
+    bound = _absbound(T, top_k, off, perm, H, W, gates, list(range(T))) + np.abs(out0)
+    check_f32(got, R, bound, K + top_k + 1, "combine %s" % (shape,))
+
+
+def test_combine_selection_weights_exact(pk, oracle_mod):
+    """Exact selection weights, dyadic activations and power-of-two gates: every term and every
+    partial sum is exact, so the result is bit-exact whatever order the atomics land in."""
+    T, top_k, E, begin, nl, K, N = 120, 3, 10, 2, 5, 64, 24
+    o = oracle_mod.default()
+    ids = pk_inputs.zipf_topk(T, E, top_k, 0.3, 171)
+    off, perm, off_d, perm_d = _device_routing(o, ids, E, begin, nl)
+    jj = np.arange(T * top_k)[:, None].astype(np.float64)
+    kk = np.arange(K)[None, :].astype(np.float64)
+    Hv = ((jj % 61) + 1.0) * 2.0 ** (kk % 8 - 4)
+    H = pk_inputs.f32_to_bf16_bits(Hv.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f64(H), Hv)
+    Wv = np.zeros((nl, K, N))
+    for e in range(nl):
+        for n in range(N):
+            Wv[e, n + (7 * e) % (K - N + 1), n] = 2.0 ** (e % 8 - 4)
+    W = pk_inputs.f32_to_bf16_bits(Wv.astype(np.float32))
+    gates = (2.0 ** -(np.arange(T * top_k) % 4)).astype(np.float32)
+    out0 = np.zeros((T, N), np.float32)
+    got = host_f32(_run(pk, T, top_k, nl, off_d, perm_d, H, W, gates, out0))
+    R = o.combine(T, top_k, off, perm, H, W, gates)
+    assert np.array_equal(got.astype(np.float64), R)
+
+
+def test_combine_concurrent_producers(pk, oracle_mod):
+    """Two combines of different local expert ranges on two streams add into one output at the
+    same time (the atomic receiving side): the result is the sum of both."""
+    T, top_k, E, K, N = 400, 4, 16, 192, 256
+    o = oracle_mod.default()
+    ids = pk_inputs.zipf_topk(T, E, top_k, 0.5, 181)
+    parts = []
+    for p, (begin, nl) in enumerate([(0, 8), (8, 8)]):
+        off, perm, off_d, perm_d = _device_routing(o, ids, E, begin, nl)
+        H = pk_inputs.normal_bf16((T * top_k, K), 1.0, 182 + p)
+        W = pk_inputs.normal_bf16((nl, K, N), 0.05, 184 + p)
+        parts.append((off, perm, off_d, perm_d, H, W, nl))
+    gates = pk_inputs.topk_gates(T, top_k, 186)
+    out = torch.zeros((T, N), device="cuda")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    keep = []
+    torch.cuda.synchronize()
+    for (off, perm, off_d, perm_d, H, W, nl), s in zip(parts, streams):
+        ws = torch.empty(pk.grouped_combine_workspace_size(nl), dtype=torch.uint8, device="cuda")
+        Hd, Wd, gd = dev_bf16(H), dev_bf16(W), torch.from_numpy(gates).cuda()
+        keep.append((ws, Hd, Wd, gd))
+        torch.cuda.synchronize()
+        pk.grouped_combine(T, top_k, off_d, perm_d, Hd, Wd, gd, out, ws, stream=s)
+    torch.cuda.synchronize()
+    R = np.zeros((T, N))
+    bound = np.zeros((T, N))
+    for off, perm, _, _, H, W, nl in parts:
+        R = o.combine(T, top_k, off, perm, H, W, gates, out0=R)
+        bound += _absbound(T, top_k, off, perm, H, W, gates, list(range(T)))
+    check_f32(host_f32(out), R, bound, K + 2 * top_k, "two producers")
+
+
+def test_combine_moe_workload_sampled(pk, oracle_mod):
+    """The MoE combine workload: 4096 tokens, top_k 8 over 256 experts (32 local, Zipf(1.1)),
+    down-projection 2048 -> 7168 per expert, output zero-initialised, in the launch configuration
+    the benchmark times; sampled tokens against the oracle."""
+    w = pk_inputs.WORKLOADS["moe_combine"]
+    o = oracle_mod.default()
+    log("MoE combine: generating inputs")
+    ids, H, W, gates = pk_inputs.combine_inputs(w)
+    off, perm, off_d, perm_d = _device_routing(o, ids, w.num_experts, w.expert_begin, w.num_local)
+    log("MoE combine: running")
+    out = _run(pk, w.tokens, w.top_k, w.num_local, off_d, perm_d, H, W, gates,
+               np.zeros((w.tokens, w.N), np.float32))
+    rng = np.random.Generator(np.random.PCG64(191))
+    tokens = sorted(set([0, w.tokens - 1]) | set(int(t) for t in rng.integers(0, w.tokens, 14)))
+    log("MoE combine: oracle on %d tokens" % len(tokens))
+    R = o.combine(w.tokens, w.top_k, off, perm, H, W, gates, tokens=tokens)[tokens]
+    bound = _absbound(w.tokens, w.top_k, off, perm, H, W, gates, tokens)
+    check_f32(host_f32(out)[tokens], R, bound, w.K + w.top_k, "MoE combine")

@@ -46,7 +46,19 @@ def test_rs_prefill_statistics():
 
 def test_workload_table():
     w = pk_inputs.WORKLOADS
-    assert set(w) == {"rs_tiny", "ag_8192", "rs_8192", "ar_16384", "moe_dispatch"}
+    assert set(w) == {"rs_tiny", "ag_8192", "rs_8192", "ar_16384", "moe_dispatch", "moe_combine"}
+    # the combine returns the dispatch workload's routing: same routing table, D 2048 -> 7168
+    c, d = w["moe_combine"], w["moe_dispatch"]
+    assert (c.tokens, c.top_k, c.num_experts, c.num_local, c.zipf_s, c.seed_route) == \
+        (d.tokens, d.top_k, d.num_experts, d.num_local, d.zipf_s, d.seed_route)
+    assert (c.K, c.N) == (d.N, d.K)
     assert (w["rs_8192"].M, w["rs_8192"].N, w["rs_8192"].K) == (8192, 8192, 1024)
     assert (w["ag_8192"].M, w["ag_8192"].N, w["ag_8192"].K) == (8192, 1024, 8192)
     assert w["rs_8192"].flops == 2.0 * 8192 * 8192 * 1024
+
+
+def test_topk_gates_sum_to_one_per_token():
+    g = pk_inputs.topk_gates(50, 8, 3).reshape(50, 8)
+    assert g.dtype == np.float32 and np.all(g > 0)
+    assert np.allclose(g.sum(axis=1), 1.0, atol=1e-6)
+    assert np.array_equal(g.reshape(-1), pk_inputs.topk_gates(50, 8, 3))
