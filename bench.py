@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="rs_8192",
-                    choices=["rs_8192", "ag_8192", "ar_16384", "moe_dispatch", "rs_tiny"])
+                    choices=["rs_8192", "ag_8192", "ar_16384", "moe_dispatch", "moe_combine",
+                             "rs_tiny"])
     ap.add_argument("--mode", default="owner", choices=["owner", "atomic"])
     ap.add_argument("--no-variant", action="store_true", help="skip the other reduce mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -154,6 +155,36 @@ def setup_workload(name, mode, torch, pk):
         nbytes = 2 * (w.M * w.K + w.K * w.N + w.M * w.N)
         desc = {"M": w.M, "N": w.N, "K": w.K, "chunks": w.chunks, "out": "bf16"}
         return step, w.flops, nbytes, desc, (chunks, Bd, C)
+    if w.kind == "combine":
+        ids, H, W, gates = pk_inputs.combine_inputs(w)
+        ids_d = torch.from_numpy(ids).cuda()
+        Hd, Wd, gd = dev(H), dev(W), torch.from_numpy(gates).cuda()
+        offsets = torch.empty(w.num_local + 1, dtype=torch.int32, device="cuda")
+        perm = torch.empty(w.tokens * w.top_k, dtype=torch.int32, device="cuda")
+        # the dispatch tables come from the library's own dispatch (a product with N = 8 that
+        # is not timed); the combine consumes them as the step after the expert FFN would
+        Xs = torch.zeros((w.tokens, 8), dtype=torch.bfloat16, device="cuda")
+        Ws = torch.zeros((w.num_local, 8, 8), dtype=torch.bfloat16, device="cuda")
+        Ys = torch.empty((w.tokens * w.top_k, 8), dtype=torch.bfloat16, device="cuda")
+        gws = torch.empty(pk.grouped_gemm_workspace_size(w.tokens, w.top_k, w.num_local),
+                          dtype=torch.uint8, device="cuda")
+        pk.grouped_gemm(ids_d, Xs, Ws, w.num_experts, w.expert_begin, offsets, perm, Ys, gws)
+        torch.cuda.synchronize()
+        del Xs, Ws, Ys, gws
+        rows = int(offsets[-1].item())
+        out = torch.zeros((w.tokens, w.N), device="cuda")
+        ws = torch.empty(pk.grouped_combine_workspace_size(w.num_local), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            pk.grouped_combine(w.tokens, w.top_k, offsets, perm, Hd, Wd, gd, out, ws)
+        flops = 2.0 * rows * w.K * w.N
+        # weights and dispatched rows once, output rows read and written once
+        nbytes = 2 * (w.num_local * w.K * w.N + rows * w.K) + 8 * w.tokens * w.N
+        desc = {"tokens": w.tokens, "D_expert": w.K, "D": w.N, "top_k": w.top_k,
+                "experts": w.num_experts, "local_experts": w.num_local, "local_rows": rows,
+                "atomic_payload_bytes": 4 * rows * w.N}
+        return step, flops, nbytes, desc, (ids_d, Hd, Wd, gd, offsets, perm, out, ws)
     # grouped
     ids, X, W = pk_inputs.moe_inputs(w)
     ids_d = torch.from_numpy(ids).cuda()
@@ -204,6 +235,27 @@ def cpu_baseline(name, target_s):
     w = pk_inputs.WORKLOADS[name]
     threads = oracle.default_threads()
     o = oracle.default()
+    if w.kind == "combine":
+        # the oracle's dispatch, then its combine for a growing prefix of tokens
+        ids, H, W, gates = pk_inputs.combine_inputs(w)
+        _, offsets, perm = o.dispatch(ids, w.num_experts, w.expert_begin, w.num_local)
+        tok_of_row = perm // w.top_k
+
+        def timed_c(n):
+            t = time.perf_counter()
+            o.combine(w.tokens, w.top_k, offsets, perm, H, W, gates, tokens=range(n),
+                      nthreads=threads)
+            return time.perf_counter() - t, int(np.sum(tok_of_row < n))
+
+        n = 16
+        dt, rows = timed_c(n)
+        if dt < target_s:
+            n = int(min(w.tokens, max(n, n * target_s / max(dt, 1e-3))))
+            dt, rows = timed_c(n)
+        flops = 2.0 * rows * w.K * w.N
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": "tokens 0..%d of %d (%d dispatched rows), K=%d, N=%d (%.1f s)"
+                          % (n - 1, w.tokens, rows, w.K, w.N, dt)}
     if w.kind == "grouped":
         # the oracle's dispatch, then its grouped product over the rows of the last experts
         # (a suffix of the expert list, grown until it takes about target_s)
