@@ -75,17 +75,11 @@ struct Cfg {
 using Cfg256x256 = Cfg<256, 256, 64, 2, 4, 2>;     // 8 waves of 128x64, 128 KB LDS
 using Cfg256x128 = Cfg<256, 128, 64, 2, 2, 3>;     // 4 waves of 128x64, 144 KB LDS
 using Cfg128x128 = Cfg<128, 128, 64, 2, 2, 2>;     // 4 waves of 64x64, 64 KB LDS
-using Cfg256x128x2 = Cfg<256, 128, 32, 2, 2, 3, 2>;  // 4 waves of 128x64, 72 KB LDS, 2 per CU
-using Cfg128x256 = Cfg<128, 256, 64, 2, 4, 3>;      // 8 waves of 64x64, 144 KB LDS
-using Cfg128x256w4 = Cfg<128, 256, 64, 1, 4, 3>;    // 4 waves of 128x64, 144 KB LDS
 
 TileShape tile_shape(TileCfgId cfg) {
     switch (cfg) {
         case CFG_256x256: return {256, 256};
         case CFG_256x128: return {256, 128};
-        case CFG_256x128_2WG: return {256, 128};
-        case CFG_128x256: return {128, 256};
-        case CFG_128x256_4W: return {128, 256};
         default: return {128, 128};
     }
 }
@@ -726,9 +720,6 @@ static hipError_t launch_cfg(const GemmArgs& a, TileCfgId cfg, Epi epi, int64_t 
         case CFG_256x256: return launch_epi<Cfg256x256, GROUPED>(a, epi, tiles, stream);
         case CFG_256x128: return launch_epi<Cfg256x128, GROUPED>(a, epi, tiles, stream);
         case CFG_128x128: return launch_epi<Cfg128x128, GROUPED>(a, epi, tiles, stream);
-        case CFG_256x128_2WG: return launch_epi<Cfg256x128x2, GROUPED>(a, epi, tiles, stream);
-        case CFG_128x256: return launch_epi<Cfg128x256, GROUPED>(a, epi, tiles, stream);
-        case CFG_128x256_4W: return launch_epi<Cfg128x256w4, GROUPED>(a, epi, tiles, stream);
         default: return hipErrorInvalidValue;
     }
 }

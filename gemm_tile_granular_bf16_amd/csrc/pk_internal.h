@@ -24,10 +24,7 @@ enum TileCfgId : int {
     CFG_256x256 = 0,  // 8 waves of 128x64, BK 64, 2 LDS stages (128 KB)
     CFG_256x128 = 1,  // 4 waves of 128x64, BK 64, 3 LDS stages (144 KB)
     CFG_128x128 = 2,  // 4 waves of 64x64, BK 64, 2 LDS stages (64 KB)
-    CFG_256x128_2WG = 3,  // 4 waves of 128x64, BK 32, 3 LDS stages (72 KB), two workgroups per CU
-    CFG_128x256 = 4,  // 8 waves of 64x64, BK 64, 3 LDS stages (144 KB)
-    CFG_128x256_4W = 5,  // 4 waves of 128x64, BK 64, 3 LDS stages (144 KB)
-    CFG_COUNT = 6
+    CFG_COUNT = 3
 };
 
 struct GemmArgs {
