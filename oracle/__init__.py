@@ -100,6 +100,9 @@ class Oracle:
         lib.pk_oracle_combine.argtypes = [i64, i32, i32, p, p, p, i64, i64, p, i64, p, p, i64, p,
                                           i32]
         lib.pk_oracle_combine.restype = i32
+        lib.pk_oracle_ring_attention.argtypes = [i64, i64, p, i64, i32, p, p, i64, i64, i64,
+                                                 ctypes.c_double, p, i64, p, i32]
+        lib.pk_oracle_ring_attention.restype = i32
         self.lib = lib
         self.path = path
 
@@ -253,6 +256,36 @@ class Oracle:
         return out
 
 
+    def ring_attention(self, Q, K_chunks, V_chunks, scale: float, nthreads: int = 0):
+        """One (batch, head) of the ring-attention local share: Q (Sq x D bf16) against the key /
+        value chunks in the given order, merged through their log-sum-exp.  Returns
+        (O binary64 Sq x D, lse binary64 Sq)."""
+        Q = _bf16(Q)
+        Ks = [_bf16(k) for k in K_chunks]
+        Vs = [_bf16(v) for v in V_chunks]
+        n = len(Ks)
+        if n != len(Vs) or n == 0:
+            raise ValueError("need matching, non-empty K and V chunk lists")
+        Sk, D = Ks[0].shape
+        for k, v in zip(Ks, Vs):
+            if k.shape != (Sk, D) or v.shape != (Sk, D):
+                raise ValueError("chunk shapes")
+        Sq = Q.shape[0]
+        if Q.shape[1] != D:
+            raise ValueError("Q has %d columns, chunks have D=%d" % (Q.shape[1], D))
+        Kp = (ctypes.c_void_p * n)(*[_ptr(k) for k in Ks])
+        Vp = (ctypes.c_void_p * n)(*[_ptr(v) for v in Vs])
+        O = np.empty((Sq, D), dtype=np.float64)
+        lse = np.empty(max(Sq, 1), dtype=np.float64)
+        rc = self.lib.pk_oracle_ring_attention(Sq, D, _ptr(Q), D, n, ctypes.cast(Kp, ctypes.c_void_p),
+                                               ctypes.cast(Vp, ctypes.c_void_p), Sk, D, D,
+                                               float(scale), _ptr(O), D, _ptr(lse),
+                                               nthreads or default_threads())
+        if rc:
+            raise RuntimeError("pk_oracle_ring_attention failed (%d)" % rc)
+        return O, lse[:Sq]
+
+
 _default = None
 
 
@@ -304,3 +337,7 @@ def combine(T, top_k, offsets, perm, H, W, gates, out0=None, tokens=None, nthrea
 
 def _load():
     return default().lib
+
+
+def ring_attention(Q, K_chunks, V_chunks, scale: float, nthreads: int = 0):
+    return default().ring_attention(Q, K_chunks, V_chunks, scale, nthreads)

@@ -16,7 +16,10 @@
  *   - token dispatch + expert GEMM: routed tokens are grouped per expert and multiplied by that
  *     expert's weight matrix;
  *   - combine (the other side of dispatch): each dispatched row's expert output is weighted by
- *     its routing gate and added back into its token's output row.
+ *     its routing gate and added back into its token's output row;
+ *   - ring attention, one rank's share: the rank's queries attend to the key/value chunks of all
+ *     ranks, one chunk at a time, and the per-chunk results are merged through their
+ *     log-sum-exp (softmax attention over the concatenated keys).
  *
  * Arithmetic: every product and sum is taken in IEEE binary64 over the bf16 inputs decoded
  * exactly; sums run in ascending index order.  bf16 outputs are the binary64 result rounded once,
@@ -298,6 +301,110 @@ int pk_oracle_combine(int64_t T, int top_k, int num_local, const int32_t* offset
             }
         }
         free(sel); free(Hs); free(Z);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* One chunk of ring attention for one (batch, head): for every query row i of Q (Sq x D bf16,
+   leading dimension ldq) against the chunk's keys K (Sk x D) and values V (Sk x D):
+       s_j = scale * sum_d Q[i][d] K[j][d]
+       lse_c = log(sum_j exp(s_j))           (computed as m + log(sum_j exp(s_j - m)), m = max_j s_j)
+       O_c[i] = sum_j exp(s_j - lse_c) V[j]
+   and the running result (O, lse) -- empty when lse[i] == -inf -- is merged with it:
+       lse' = log(exp(lse) + exp(lse_c)),  O' = exp(lse - lse') O + exp(lse_c - lse') O_c.
+   O is Sq x D binary64 (leading dimension ldo), lse is Sq binary64; both in/out. */
+static void attn_chunk_rows(int64_t r0, int64_t r1, int64_t Sk, int64_t D, const uint16_t* Q,
+                            int64_t ldq, const uint16_t* K, int64_t ldk, const uint16_t* V,
+                            int64_t ldv, double scale, double* O, int64_t ldo, double* lse,
+                            double* s, double* oc) {
+    for (int64_t i = r0; i < r1; ++i) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j < Sk; ++j) {
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                acc += pk_oracle_bf16_to_f64(Q[i * ldq + d]) * pk_oracle_bf16_to_f64(K[j * ldk + d]);
+            s[j] = scale * acc;
+            if (s[j] > m) m = s[j];
+        }
+        double sum = 0.0;
+        for (int64_t j = 0; j < Sk; ++j) sum += exp(s[j] - m);
+        const double lse_c = m + log(sum);
+        for (int64_t d = 0; d < D; ++d) oc[d] = 0.0;
+        for (int64_t j = 0; j < Sk; ++j) {
+            const double p = exp(s[j] - lse_c);
+            for (int64_t d = 0; d < D; ++d) oc[d] += p * pk_oracle_bf16_to_f64(V[j * ldv + d]);
+        }
+        double* o = O + i * ldo;
+        if (lse[i] == -INFINITY) {
+            for (int64_t d = 0; d < D; ++d) o[d] = oc[d];
+            lse[i] = lse_c;
+        } else {
+            const double hi = lse[i] > lse_c ? lse[i] : lse_c;
+            const double merged = hi + log(exp(lse[i] - hi) + exp(lse_c - hi));
+            const double a = exp(lse[i] - merged), b = exp(lse_c - merged);
+            for (int64_t d = 0; d < D; ++d) o[d] = a * o[d] + b * oc[d];
+            lse[i] = merged;
+        }
+    }
+}
+
+typedef struct {
+    int64_t r0, r1, Sk, D;
+    const uint16_t *Q, *K, *V;
+    int64_t ldq, ldk, ldv, ldo;
+    double scale;
+    double *O, *lse;
+    int rc;
+} attn_job;
+
+static void* attn_rows_thread(void* arg) {
+    attn_job* j = (attn_job*)arg;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(j->Sk > 0 ? j->Sk : 1));
+    double* oc = (double*)malloc(sizeof(double) * (size_t)(j->D > 0 ? j->D : 1));
+    if (!s || !oc) { j->rc = 2; free(s); free(oc); return NULL; }
+    attn_chunk_rows(j->r0, j->r1, j->Sk, j->D, j->Q, j->ldq, j->K, j->ldk, j->V, j->ldv, j->scale,
+                    j->O, j->ldo, j->lse, s, oc);
+    free(s); free(oc);
+    j->rc = 0;
+    return NULL;
+}
+
+/* Ring-attention local share for one (batch, head): the chunks are visited in the given order
+   (chunk c = K_chunks[c], V_chunks[c], Sk_chunk rows each, leading dimensions ldk / ldv), each
+   merged into (O, lse) as above.  O (Sq x D, ldo) and lse (Sq) are outputs (initialised here to
+   the empty result).  Query rows are split over threads. */
+int pk_oracle_ring_attention(int64_t Sq, int64_t D, const uint16_t* Q, int64_t ldq,
+                             int num_chunks, const uint16_t* const* K_chunks,
+                             const uint16_t* const* V_chunks, int64_t Sk_chunk, int64_t ldk,
+                             int64_t ldv, double scale, double* O, int64_t ldo, double* lse,
+                             int nthreads) {
+    if (Sq < 0 || D < 0 || num_chunks < 0 || Sk_chunk < 0) return 1;
+    for (int64_t i = 0; i < Sq; ++i) {
+        lse[i] = -INFINITY;
+        for (int64_t d = 0; d < D; ++d) O[i * ldo + d] = 0.0;
+    }
+    int nt = resolve_threads(nthreads, Sq);
+    for (int c = 0; c < num_chunks; ++c) {
+        attn_job jobs[256];
+        pthread_t tid[256];
+        int started[256];
+        int64_t per = (Sq + nt - 1) / nt;
+        int used = 0;
+        for (int t = 0; t < nt; ++t) {
+            int64_t b = t * per, e = b + per < Sq ? b + per : Sq;
+            if (b >= e) break;
+            jobs[t] = (attn_job){b, e, Sk_chunk, D, Q, K_chunks[c], V_chunks[c], ldq, ldk, ldv, ldo,
+                                 scale, O, lse, 1};
+            started[t] = pthread_create(&tid[t], NULL, attn_rows_thread, &jobs[t]) == 0;
+            if (!started[t]) attn_rows_thread(&jobs[t]);
+            ++used;
+        }
+        int rc = 0;
+        for (int t = 0; t < used; ++t) {
+            if (started[t]) pthread_join(tid[t], NULL);
+            if (jobs[t].rc) rc = jobs[t].rc;
+        }
         if (rc) return rc;
     }
     return 0;

@@ -474,4 +474,86 @@ def pin_combine_token_subset(o):
 
 COMBINE_PINS = [pin_combine_selection_weights, pin_combine_brute_force, pin_combine_token_subset]
 
-ALL_PINS = BF16_PINS + GEMM_PINS + REDUCE_PINS + DISPATCH_PINS + GROUPED_PINS + COMBINE_PINS
+def pin_attention_uniform_scores(o):
+    """Q = 0 makes every score 0: the softmax is uniform over all keys of all chunks, so O is the
+    exact mean of the value rows and lse = log(number of keys)."""
+    Sq, D, Sk, n = 4, 16, 6, 3
+    Q = np.zeros((Sq, D), dtype=np.uint16)
+    Ks = [pk_inputs.normal_bf16((Sk, D), 1.0, 201 + c) for c in range(n)]
+    Vs = [pk_inputs.normal_bf16((Sk, D), 1.0, 211 + c) for c in range(n)]
+    O, lse = o.ring_attention(Q, Ks, Vs, 0.125)
+    allv = np.concatenate([bf16_bits_to_f64(v) for v in Vs])
+    for d in range(D):
+        mean = sum(Fraction(x) for x in allv[:, d]) / (Sk * n)
+        for i in range(Sq):
+            assert abs(Fraction(O[i, d]) - mean) <= Fraction(2.0 ** -48) * (1 + abs(mean))
+    assert np.allclose(lse, np.log(Sk * n), rtol=0, atol=1e-15)
+
+
+def pin_attention_one_hot(o):
+    """Query i points at exactly one key (one-hot rows, a huge scale): every other weight
+    underflows to zero, so O[i] is that key's value row bit for bit and lse is its score."""
+    D, Sk, n = 16, 5, 4
+    keys = [(c, j) for c in range(n) for j in range(Sk)]
+    K = np.zeros((n * Sk, D))
+    for idx in range(n * Sk):
+        K[idx, idx % D] = 1.0 + (idx // D)          # distinct (column, magnitude) per key
+    picks = [0, 7, 13, 19, 11]
+    Q = np.zeros((len(picks), D))
+    for i, idx in enumerate(picks):
+        Q[i, idx % D] = 1.0
+    scale = 4096.0
+    Kb, Qb = _bits(K), _bits(Q)
+    Vs = [pk_inputs.normal_bf16((Sk, D), 1.0, 221 + c) for c in range(n)]
+    O, lse = o.ring_attention(Qb, [Kb[c * Sk:(c + 1) * Sk] for c in range(n)], Vs, scale)
+    allv = np.concatenate([bf16_bits_to_f64(v) for v in Vs])
+    for i, idx in enumerate(picks):
+        col, mag = idx % D, 1.0 + idx // D
+        best = max(range(n * Sk), key=lambda j: K[j, col])  # the strongest key in that column
+        assert np.array_equal(O[i], allv[best]), (i, idx, best)
+        assert lse[i] == scale * K[best, col]
+    del keys
+
+
+def pin_attention_two_keys_logistic(o):
+    """Two keys in two chunks: the weights are the logistic function of the score difference,
+    p = 1 / (1 + exp(s2 - s1)), so O = p V1 + (1 - p) V2 and lse = s1 + log1p(exp(s2 - s1))."""
+    D = 8
+    Q = pk_inputs.normal_bf16((3, D), 1.0, 231)
+    K1, K2 = pk_inputs.normal_bf16((1, D), 1.0, 232), pk_inputs.normal_bf16((1, D), 1.0, 233)
+    V1, V2 = pk_inputs.normal_bf16((1, D), 1.0, 234), pk_inputs.normal_bf16((1, D), 1.0, 235)
+    scale = 0.5
+    O, lse = o.ring_attention(Q, [K1, K2], [V1, V2], scale)
+    q, k1, k2 = bf16_bits_to_f64(Q), bf16_bits_to_f64(K1)[0], bf16_bits_to_f64(K2)[0]
+    v1, v2 = bf16_bits_to_f64(V1)[0], bf16_bits_to_f64(V2)[0]
+    for i in range(3):
+        s1 = scale * float(sum(Fraction(a) * Fraction(b) for a, b in zip(q[i], k1)))
+        s2 = scale * float(sum(Fraction(a) * Fraction(b) for a, b in zip(q[i], k2)))
+        p = 1.0 / (1.0 + np.exp(s2 - s1))
+        assert np.allclose(O[i], p * v1 + (1.0 - p) * v2, rtol=1e-14, atol=1e-15)
+        assert abs(lse[i] - (s1 + np.log1p(np.exp(s2 - s1)))) <= 1e-14 * (1 + abs(lse[i]))
+
+
+def pin_attention_chunking_invariance(o):
+    """The log-sum-exp merge is exact up to rounding: splitting the keys into chunks differently
+    or visiting the chunks in another order gives the same O and lse (binary64 rounding only)."""
+    Sq, D, S = 6, 32, 24
+    Q = pk_inputs.normal_bf16((Sq, D), 1.0, 241)
+    K = pk_inputs.normal_bf16((S, D), 1.0, 242)
+    V = pk_inputs.normal_bf16((S, D), 1.0, 243)
+    one = o.ring_attention(Q, [K], [V], 0.3)
+    for parts in ([8, 8, 8], [12, 12], [4, 4, 4, 4, 4, 4]):
+        edges = np.cumsum([0] + parts)
+        Ks = [K[edges[c]:edges[c + 1]] for c in range(len(parts))]
+        Vs = [V[edges[c]:edges[c + 1]] for c in range(len(parts))]
+        for order in (list(range(len(parts))), list(reversed(range(len(parts))))):
+            O, lse = o.ring_attention(Q, [Ks[c] for c in order], [Vs[c] for c in order], 0.3)
+            assert np.allclose(O, one[0], rtol=0, atol=1e-13)
+            assert np.allclose(lse, one[1], rtol=0, atol=1e-13)
+
+
+ATTENTION_PINS = [pin_attention_uniform_scores, pin_attention_one_hot,
+                  pin_attention_two_keys_logistic, pin_attention_chunking_invariance]
+
+ALL_PINS = (BF16_PINS + GEMM_PINS + REDUCE_PINS + DISPATCH_PINS + GROUPED_PINS + COMBINE_PINS
+            + ATTENTION_PINS)

@@ -2,7 +2,8 @@
 (compiled here, on the CPU) must fail at least one pin.  Mistakes cover a dropped term, a sign, an
 index/transposition, the rounding rule, dispatch stability and range checks, the gathered row,
 the expert weight choice, the destination term of the reduction, and the gate, token and
-accumulation of the combine."""
+accumulation of the combine, and the
+scale, max shift, key index and merge of the attention."""
 import os
 
 import pytest
@@ -43,6 +44,16 @@ MUTANTS = [
      "const double g = (double)gates[sel[i]];", _pins.COMBINE_PINS),
     ("combine_overwrite", "for (int64_t c = 0; c < N; ++c) o[c] += g * z[c];",
      "for (int64_t c = 0; c < N; ++c) o[c] = g * z[c];", _pins.COMBINE_PINS),
+    ("attn_no_rescale", "for (int64_t d = 0; d < D; ++d) o[d] = a * o[d] + b * oc[d];",
+     "for (int64_t d = 0; d < D; ++d) o[d] = o[d] + b * oc[d];", _pins.ATTENTION_PINS),
+    ("attn_drop_scale", "s[j] = scale * acc;", "s[j] = acc;", _pins.ATTENTION_PINS),
+    ("attn_no_max_shift", "for (int64_t j = 0; j < Sk; ++j) sum += exp(s[j] - m);\n        const double lse_c = m + log(sum);",
+     "for (int64_t j = 0; j < Sk; ++j) sum += exp(s[j]);\n        const double lse_c = log(sum);",
+     _pins.ATTENTION_PINS),
+    ("attn_transposed_k", "pk_oracle_bf16_to_f64(K[j * ldk + d])", "pk_oracle_bf16_to_f64(K[(d % Sk) * ldk + (j % D)])",
+     _pins.ATTENTION_PINS),
+    ("attn_merge_weight", "const double a = exp(lse[i] - merged), b = exp(lse_c - merged);",
+     "const double a = exp(lse[i] - merged), b = exp(lse_c - lse[i]);", _pins.ATTENTION_PINS),
 ]
 
 
