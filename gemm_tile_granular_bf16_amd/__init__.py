@@ -65,6 +65,9 @@ def library() -> ctypes.CDLL:
     lib.pk_grouped_combine.restype = i32
     lib.pk_grouped_combine_workspace_size.argtypes = [i32]
     lib.pk_grouped_combine_workspace_size.restype = sz
+    lib.pk_ring_attention.argtypes = [i64, i64, i64, p, i64, i64, p, p, i32, i64, i32, i64, i64,
+                                      i64, i64, ctypes.c_float, p, i64, i64, i32, p, i64, p]
+    lib.pk_ring_attention.restype = i32
     lib.pk_status_string.argtypes = [i32]
     lib.pk_status_string.restype = ctypes.c_char_p
     lib.pk_last_error.argtypes = []
@@ -163,6 +166,60 @@ def gemm_reduce(A: torch.Tensor, B: torch.Tensor, D: Union[torch.Tensor, Sequenc
                                     shards[0].size(0), lds.pop(), mode, op, ldo,
                                     _stream_handle(stream)))
     return D
+
+
+def _bhsd(t: torch.Tensor, dtypes, what: str):
+    """(BH, S, D) device tensor with unit stride along D: (pointer, bh stride, row stride)."""
+    if t.dim() != 3 or not t.is_cuda or t.dtype not in dtypes or t.stride(2) != 1:
+        raise TypeError("%s must be a BH x S x D device tensor of %s with unit stride along D"
+                        % (what, "/".join(str(d) for d in dtypes)))
+    return t.data_ptr(), t.stride(0), t.stride(1)
+
+
+def ring_attention(Q: torch.Tensor, K_chunks, V_chunks, O: torch.Tensor,
+                   lse: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                   first_chunk: int = 0, stream=None):
+    """One rank's share of ring attention (pk_ring_attention): ``Q`` (BH x Sq x 128 bf16)
+    against the key/value chunks (lists of BH x chunk_len x 128 bf16, all the same length),
+    visited from ``first_chunk`` on and merged through their log-sum-exp.  Writes ``O``
+    (BH x Sq x 128, bf16 or fp32) and, if given, ``lse`` (BH x Sq fp32).  ``scale`` defaults to
+    1/sqrt(128)."""
+    qp, q_bh, ldq = _bhsd(Q, _BF16_LIKE, "Q")
+    BH, Sq, D = Q.shape
+    if len(K_chunks) != len(V_chunks) or not K_chunks:
+        raise ValueError("need matching, non-empty key and value chunk lists")
+    n = len(K_chunks)
+    if n > PK_MAX_PARTS:
+        raise ValueError("at most %d chunks" % PK_MAX_PARTS)
+    k0, v0 = K_chunks[0], V_chunks[0]
+    _, k_bh, ldk = _bhsd(k0, _BF16_LIKE, "K chunk")
+    _, v_bh, ldv = _bhsd(v0, _BF16_LIKE, "V chunk")
+    chunk_len = k0.size(1)
+    for k, v in zip(K_chunks, V_chunks):
+        for t, ref, what in ((k, k0, "K"), (v, v0, "V")):
+            _bhsd(t, _BF16_LIKE, what + " chunk")
+            if tuple(t.shape) != (BH, chunk_len, D) or t.stride() != ref.stride():
+                raise ValueError("every %s chunk must be %d x %d x %d with the same strides"
+                                 % (what, BH, chunk_len, D))
+    op, o_bh, ldo = _bhsd(O, (torch.bfloat16, torch.float32), "O")
+    if tuple(O.shape) != (BH, Sq, D):
+        raise ValueError("O must be %d x %d x %d" % (BH, Sq, D))
+    lp, lse_bh = None, 0
+    if lse is not None:
+        if lse.dim() != 2 or not lse.is_cuda or lse.dtype != torch.float32 or lse.stride(1) != 1 \
+                or tuple(lse.shape) != (BH, Sq):
+            raise TypeError("lse must be a BH x Sq fp32 device tensor with unit row stride")
+        lp, lse_bh = lse.data_ptr(), lse.stride(0)
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    Kp = (ctypes.c_void_p * n)(*[k.data_ptr() for k in K_chunks])
+    Vp = (ctypes.c_void_p * n)(*[v.data_ptr() for v in V_chunks])
+    _check(library().pk_ring_attention(BH, Sq, D, qp, q_bh, ldq, ctypes.cast(Kp, ctypes.c_void_p),
+                                       ctypes.cast(Vp, ctypes.c_void_p), n, chunk_len, first_chunk,
+                                       k_bh, ldk, v_bh, ldv, float(scale), op, o_bh, ldo,
+                                       PK_BF16 if O.dtype == torch.bfloat16 else PK_F32, lp, lse_bh,
+                                       _stream_handle(stream)))
+    return O, lse
 
 
 def grouped_combine_workspace_size(num_local: int) -> int:

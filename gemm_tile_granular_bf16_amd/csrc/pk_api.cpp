@@ -347,4 +347,54 @@ pk_status pk_grouped_combine(int64_t T, int top_k, int num_local, const int32_t*
                       "pk_grouped_combine launch");
 }
 
+pk_status pk_ring_attention(int64_t BH, int64_t Sq, int64_t D, const uint16_t* Q, int64_t q_bh,
+                            int64_t ldq, const uint16_t* const K_chunks[],
+                            const uint16_t* const V_chunks[], int num_chunks, int64_t chunk_len,
+                            int first_chunk, int64_t k_bh, int64_t ldk, int64_t v_bh, int64_t ldv,
+                            float scale, void* O, int64_t o_bh, int64_t ldo, pk_dtype o_dtype,
+                            float* lse, int64_t lse_bh, void* stream) {
+    if (BH < 0 || Sq < 0 || D < 0 || chunk_len < 0) return fail(PK_ERR_INVALID_ARGUMENT, "negative size");
+    if (o_dtype != PK_BF16 && o_dtype != PK_F32) return fail(PK_ERR_INVALID_ARGUMENT, "o_dtype");
+    if (num_chunks < 1 || num_chunks > PK_MAX_PARTS)
+        return fail(PK_ERR_INVALID_ARGUMENT, "num_chunks %d outside 1..%d", num_chunks, PK_MAX_PARTS);
+    if (first_chunk < 0 || first_chunk >= num_chunks)
+        return fail(PK_ERR_INVALID_ARGUMENT, "first_chunk outside [0, num_chunks)");
+    if (BH == 0 || Sq == 0) return ok();
+    if (chunk_len == 0) return fail(PK_ERR_INVALID_ARGUMENT, "no keys: softmax over an empty set");
+    if (!Q || !K_chunks || !V_chunks || !O) return fail(PK_ERR_INVALID_ARGUMENT, "null pointer");
+    for (int c = 0; c < num_chunks; ++c)
+        if (!K_chunks[c] || !V_chunks[c]) return fail(PK_ERR_INVALID_ARGUMENT, "null chunk %d", c);
+    if (ldq < D || ldk < D || ldv < D || ldo < D)
+        return fail(PK_ERR_INVALID_ARGUMENT, "leading dimension too small");
+    if ((BH > 1 && (q_bh < Sq * ldq || k_bh < chunk_len * ldk || v_bh < chunk_len * ldv ||
+                    o_bh < Sq * ldo)) || (lse && BH > 1 && lse_bh < Sq))
+        return fail(PK_ERR_INVALID_ARGUMENT, "batch*head strides overlap");
+    if (!(scale == scale)) return fail(PK_ERR_INVALID_ARGUMENT, "scale is NaN");
+    if (D != pk::ring_attention_head_dim())
+        return fail(PK_ERR_UNSUPPORTED, "head dimension %lld (supported: %d)", (long long)D,
+                    pk::ring_attention_head_dim());
+    if (chunk_len % pk::ring_attention_block_keys())
+        return fail(PK_ERR_UNSUPPORTED, "chunk_len must be a multiple of %d",
+                    pk::ring_attention_block_keys());
+    if (ldq % 8 || ldk % 8 || ldv % 8 || q_bh % 8 || k_bh % 8 || v_bh % 8 ||
+        (o_dtype == PK_BF16 ? (ldo % 8 || o_bh % 8) : (ldo % 4 || o_bh % 4)))
+        return fail(PK_ERR_UNSUPPORTED, "strides must be 16-byte multiples");
+    if (!aligned16(Q) || !aligned16(O)) return fail(PK_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+    for (int c = 0; c < num_chunks; ++c)
+        if (!aligned16(K_chunks[c]) || !aligned16(V_chunks[c]))
+            return fail(PK_ERR_UNSUPPORTED, "chunk %d not 16-byte aligned", c);
+    if (BH * ((Sq + 255) / 256) > INT32_MAX / 2) return fail(PK_ERR_UNSUPPORTED, "too many query tiles");
+
+    pk::AttnArgs a{};
+    a.BH = BH; a.Sq = Sq; a.chunk_len = chunk_len;
+    a.num_chunks = num_chunks; a.first_chunk = first_chunk;
+    a.Q = Q; a.q_bh = q_bh; a.ldq = ldq;
+    for (int c = 0; c < num_chunks; ++c) { a.K[c] = K_chunks[c]; a.V[c] = V_chunks[c]; }
+    a.k_bh = k_bh; a.ldk = ldk; a.v_bh = v_bh; a.ldv = ldv;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.O = O; a.o_bh = o_bh; a.ldo = ldo; a.o_f32 = o_dtype == PK_F32;
+    a.lse = lse; a.lse_bh = lse_bh;
+    return hip_status(pk::launch_ring_attention(a, (hipStream_t)stream), "pk_ring_attention launch");
+}
+
 }  // extern "C"

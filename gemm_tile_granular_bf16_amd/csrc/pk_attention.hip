@@ -1,0 +1,295 @@
+// Ring attention, one rank's share, for gfx950.
+//
+// In sequence parallelism with ring attention ("Loads and Loads of Fluffy Kittens" summary, Key
+// claims and Results: Ring Attention, B=16, D=128), a rank keeps its block of queries while the
+// key/value blocks of all ranks pass by; it attends to each block as it arrives and merges the
+// partial results through their log-sum-exp.  Merging per key block is also exactly what a
+// streaming (online) softmax does, so one rank's share is computed here in one pass over the
+// chunks, in the order given (the rank's own chunk first), with the running state in registers:
+//
+//   per query row: m = running max of the scaled scores (log2 units), l = running sum of
+//   exp2(score - m), O = running sum of exp2(score - m) * V; a new key block with block max mb
+//   rescales l and O by exp2(m - max(m, mb)) and adds its own terms.  At the end O / l is the
+//   output and (m + log2 l) * ln 2 its log-sum-exp.
+//
+// Kernel structure (one workgroup = 8 waves = 256 query rows of one (batch, head), 32 per wave):
+//  * the wave's Q block (32 x 128 bf16) stays in registers as MFMA operands for the whole pass;
+//  * key/value blocks of 64 rows go HBM -> LDS with direct 16-byte DMA, ST-stage pipeline, one
+//    barrier per block (the same protocol as the GEMM main loop);
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the first operand, Q as the second)
+//    leaves every lane holding one query row, so the row max / row sum need only a swap with the
+//    lane 32 away (v_permlane32_swap) and the O rescale needs no cross-lane traffic at all;
+//  * O^T += V^T P^T: V^T comes from LDS with transposing reads (ds_read_b64_tr_b16), P from the
+//    S registers converted to bf16.  The MFMA k order is chosen to match the keys each lane
+//    already holds (4 + 4 keys per lane per 16-key slice), so P needs no shuffling: V^T's rows
+//    are read in the same order.  P is carried as the sum of two bf16 terms (hi + lo), which keeps
+//    the probabilities to ~16 significant bits at the price of a second PV MFMA.
+//  * LDS rows are 256 bytes (128 bf16); the 16-byte chunk index is XORed with row % 16 for K
+//    (16 rows per read phase) and with 2 * (row % 8) for V (4 rows x 2 chunks per read phase).
+#include "pk_device.h"
+#include "pk_internal.h"
+
+namespace pk {
+
+namespace {
+
+constexpr int kD = 128;                  // head dimension
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBM = kWaves * 32;         // query rows per workgroup
+constexpr int kBN = 64;                  // keys per block
+constexpr int kRowBytes = kD * 2;        // 256
+constexpr int kTileBytes = kBN * kRowBytes;   // 16 KB (K or V block)
+constexpr int kStageBytes = 2 * kTileBytes;   // K then V
+constexpr int kST = 3;                   // LDS stages
+constexpr int kLPS = 2 * (kTileBytes / 1024 / kWaves);  // DMA instructions per wave per block (4)
+
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 7) << 1; }
+
+// fp32 pair -> packed bf16 pair (round to nearest even, hardware convert)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// table[i] for a wave-uniform i, with a chain of selects
+__device__ __forceinline__ const uint16_t* pick_attn(const uint16_t* const (&table)[PK_MAX_PARTS], int i) {
+    const uint16_t* r = table[0];
+#pragma unroll
+    for (int j = 1; j < PK_MAX_PARTS; ++j) r = (i == j) ? table[j] : r;
+    return r;
+}
+
+// value of x at lane l and at lane l ^ 32, in either order
+__device__ __forceinline__ void partner_pair(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p) {
+    __shared__ __attribute__((aligned(1024))) char lds[kST * kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;   // lane half
+    const int q32 = lane & 31;
+
+    // ---- which (batch*head, query tile) --------------------------------------------------------
+    const int n_qt = (int)((p.Sq + kBM - 1) / kBM);
+    int L;
+    if (!xcd_remap(blockIdx.x, (int)(p.BH * n_qt), L)) return;
+    const int64_t bh = L / n_qt;
+    const int64_t q_tile0 = (int64_t)(L - bh * n_qt) * kBM;
+    const int64_t qrow = q_tile0 + w * 32 + q32;       // this lane's query row
+    const bool q_ok = qrow < p.Sq;
+    const int64_t qrow_ld = q_ok ? qrow : p.Sq - 1;      // clamped for loads
+
+    // ---- Q fragments (second MFMA operand of S^T = K Q^T): 8 consecutive d per 16-d slice ----
+    bf16x8 qf[kD / 16];
+    {
+        const uint16_t* qsrc = p.Q + bh * p.q_bh + qrow_ld * p.ldq + 8 * h;
+#pragma unroll
+        for (int kk = 0; kk < kD / 16; ++kk) qf[kk] = *(const bf16x8*)(qsrc + 16 * kk);
+    }
+
+    // ---- key/value block schedule ------------------------------------------------------------
+    const int64_t nb_chunk = p.chunk_len / kBN;
+    const int64_t nb = nb_chunk * p.num_chunks;
+    // DMA: K (and V) block = 16 KB = 16 one-KB blocks; wave w moves blocks w and w + 8; lane i
+    // fills LDS row 4*b + i/16, 16-byte position i%16.
+    int dma_row[2], dma_ck[2], dma_cv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int b = j * kWaves + w;
+        const int row = 4 * b + (lane >> 4);
+        const int pos = lane & 15;
+        dma_row[j] = row;
+        dma_ck[j] = pos ^ swz_k(row);  // global chunk this lane fetches into position pos
+        dma_cv[j] = pos ^ swz_v(row);
+    }
+    auto issue = [&](int64_t blk, int slot) {
+        const int64_t c = (p.first_chunk + blk / nb_chunk) % p.num_chunks;
+        const int64_t krow0 = (blk % nb_chunk) * kBN;
+        const uint16_t* kb = pick_attn(p.K, (int)c) + bh * p.k_bh + krow0 * p.ldk;
+        const uint16_t* vb = pick_attn(p.V, (int)c) + bh * p.v_bh + krow0 * p.ldv;
+        char* sk = lds + slot * kStageBytes;
+        char* sv = sk + kTileBytes;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int b = j * kWaves + w;
+            dma16(kb + (int64_t)dma_row[j] * p.ldk + dma_ck[j] * 8, sk + b * 1024);
+            dma16(vb + (int64_t)dma_row[j] * p.ldv + dma_cv[j] * 8, sv + b * 1024);
+        }
+    };
+
+    // ---- LDS read offsets ----------------------------------------------------------------------
+    // K operand of key block kb (32 keys), d-slice kk: row kb*32 + lane%32, chunk 2*kk + lane/32.
+    int k_off[2][kD / 16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + q32;
+#pragma unroll
+        for (int kk = 0; kk < kD / 16; ++kk)
+            k_off[kb][kk] = row * kRowBytes + (((2 * kk + h) ^ swz_k(row)) << 4);
+    }
+    // V^T operand of d-block db, 16-key slice t: two transposing reads of 4 key rows each, rows
+    // 16t + 4*(G/2) + (i/4) (lo) and 16t + 8 + 4*(G/2) + (i/4) (hi), columns
+    // db*32 + 16*(G%2) + 4*(i%4) .. +3, for lane i of 16-lane group G.
+    const int G = lane >> 4, i16 = lane & 15;
+    int v_lo_row[4], v_hi_row[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        v_lo_row[t] = 16 * t + 4 * (G >> 1) + (i16 >> 2);
+        v_hi_row[t] = v_lo_row[t] + 8;
+    }
+    auto v_off = [&](int row, int db) {
+        const int d0 = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+        return row * kRowBytes + ((((d0 >> 3)) ^ swz_v(row)) << 4) + (d0 & 7) * 2;
+    };
+
+    // ---- running state -------------------------------------------------------------------------
+    f32x16 oacc[kD / 32];
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    const float sl2 = p.scale_log2;
+
+    auto process = [&](int slot) {
+        const char* sk = lds + slot * kStageBytes;
+        const char* sv = sk + kTileBytes;
+        // S^T: lane = query, 16 keys per 32-key block
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < kD / 16; ++kk) {
+                const bf16x8 kf = *(const bf16x8*)(sk + k_off[kb][kk]);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
+            }
+        }
+        // online softmax update (log2 units)
+        float mb = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[kb][r] *= sl2;
+                mb = fmaxf(mb, sacc[kb][r]);
+            }
+        float ma, mc;
+        partner_pair(mb, ma, mc);
+        const float m_new = fmaxf(m_run, fmaxf(ma, mc));
+        // exp2 of an exact 0 is taken as exactly 1 (the hardware exp2 is only faithful): a block
+        // that does not raise the max leaves O and l untouched, and the maximal key weighs 1
+        const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        float rs = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float d = sacc[kb][r] - m_new;
+                sacc[kb][r] = d == 0.0f ? 1.0f : __builtin_amdgcn_exp2f(d);
+                rs += sacc[kb][r];
+            }
+        float ra, rc;
+        partner_pair(rs, ra, rc);
+        l_run = l_run * alpha + (ra + rc);
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        // P = hi + lo in bf16: per 16-key slice t, registers 8*(t%2) .. +7 of block t/2
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int kb = t >> 1, r0 = 8 * (t & 1);
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = sacc[kb][r0 + 2 * e], b = sacc[kb][r0 + 2 * e + 1];
+                hi[e] = pack_bf16(a, b);
+                lo[e] = pack_bf16(a - bf16_lo_to_f32(hi[e]), b - bf16_hi_to_f32(hi[e]));
+            }
+            const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+            const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db) {
+                const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    PK_LDS_PTR(i16x4, sv + v_off(v_lo_row[t], db)));
+                const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    PK_LDS_PTR(i16x4, sv + v_off(v_hi_row[t], db)));
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi, oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo, oacc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- pipeline over the key/value blocks (same protocol as the GEMM main loop) -------------
+#pragma unroll
+    for (int s = 0; s < kST - 1; ++s)
+        if (s < nb) issue(s, s);
+    for (int64_t blk = 0; blk < nb; ++blk) {
+        // block blk has landed (later blocks may still be in flight), and every wave is done
+        // with the slot about to be refilled
+        if (blk + 1 < nb && kST >= 3) wait_vmcnt<kLPS>(); else wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+        if (blk + kST - 1 < nb) issue(blk + kST - 1, (int)((blk + kST - 1) % kST));
+        process((int)(blk % kST));
+    }
+
+    // ---- output: O = O^T / l, lane = query row, 4 consecutive d per register group -------------
+    if (!q_ok) return;
+    const float inv_l = 1.0f / l_run;
+    if (p.o_f32) {
+        float* orow = (float*)p.O + bh * p.o_bh + qrow * p.ldo;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4_t v = {oacc[db][4 * g] * inv_l, oacc[db][4 * g + 1] * inv_l,
+                                   oacc[db][4 * g + 2] * inv_l, oacc[db][4 * g + 3] * inv_l};
+                *(f32x4_t*)(orow + db * 32 + 8 * g + 4 * h) = v;
+            }
+    } else {
+        uint16_t* orow = (uint16_t*)p.O + bh * p.o_bh + qrow * p.ldo;
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 v;
+                v[0] = bf16_rne(oacc[db][4 * g] * inv_l) | (bf16_rne(oacc[db][4 * g + 1] * inv_l) << 16);
+                v[1] = bf16_rne(oacc[db][4 * g + 2] * inv_l) | (bf16_rne(oacc[db][4 * g + 3] * inv_l) << 16);
+                *(u32x2*)(orow + db * 32 + 8 * g + 4 * h) = v;
+            }
+    }
+    if (p.lse && h == 0)
+        p.lse[bh * p.lse_bh + qrow] = (m_run + __builtin_log2f(l_run)) * 0.69314718055994531f;
+}
+
+hipError_t launch_ring_attention(const AttnArgs& a, hipStream_t stream) {
+    const int64_t n_qt = (a.Sq + kBM - 1) / kBM;
+    const int64_t blocks = a.BH * n_qt;
+    if (blocks <= 0) return hipSuccess;
+    const int64_t grid = (blocks + 7) / 8 * 8;
+    hipLaunchKernelGGL(ring_attention_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+int ring_attention_block_keys() { return kBN; }
+int ring_attention_head_dim() { return kD; }
+
+}  // namespace pk

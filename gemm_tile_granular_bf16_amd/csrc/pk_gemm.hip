@@ -37,18 +37,11 @@
 //    of tile rows, so operand panels are reused from that XCD's L2.
 #include <type_traits>
 
+#include "pk_device.h"
 #include "pk_internal.h"
 
 namespace pk {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-#define PK_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int ST_, int WG_PER_CU_ = 1>
 struct Cfg {
@@ -99,28 +92,6 @@ __device__ __forceinline__ int swz_a(int row) {
 template <int CPRB>
 __device__ __forceinline__ int swz_b(int k) { return (10 * (k & 3)) & (CPRB - 1); }
 
-// 16 bytes per lane HBM -> LDS; lane i lands at lds_base + 16*i (lds_base is wave-uniform).
-__device__ __forceinline__ void dma16(const void* src, char* lds_base) {
-    __builtin_amdgcn_global_load_lds(src, PK_LDS_PTR(void, lds_base), 16, 0, 0);
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0]+[15:14], expcnt[6:4],
-// lgkmcnt[11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
-
-// Round to nearest even, fp32 -> bf16 bits (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
 // Pick table[i] with a chain of selects (keeps kernel-argument tables out of scratch memory).
 template <typename T>
 __device__ __forceinline__ T pick(const T (&table)[PK_MAX_PARTS], int i) {
@@ -128,18 +99,6 @@ __device__ __forceinline__ T pick(const T (&table)[PK_MAX_PARTS], int i) {
 #pragma unroll
     for (int j = 1; j < PK_MAX_PARTS; ++j) r = (i == j) ? table[j] : r;
     return r;
-}
-
-// Hardware block id -> logical tile id.  Blocks are dealt to the 8 XCDs round-robin
-// (block b runs on XCD b % 8); XCD x receives logical tiles [x*q + min(x, r), ...) in launch
-// order, so neighbouring logical tiles share an L2.  Returns false for surplus blocks.
-__device__ __forceinline__ bool xcd_remap(int b, int total, int& L) {
-    const int x = b & 7, s = b >> 3;
-    const int q = total >> 3, r = total & 7;
-    const int cnt = q + (x < r ? 1 : 0);
-    if (s >= cnt) return false;
-    L = x * q + (x < r ? x : r) + s;
-    return true;
 }
 
 // ------------------------------------------------------------------------------------------------

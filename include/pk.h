@@ -14,7 +14,9 @@
  *   pk_grouped_gemm  -- token dispatch (stable grouping of routed slots per local expert) followed
  *                       by the per-expert product over the gathered rows;
  *   pk_grouped_combine -- the per-expert down-projection of the dispatched rows, weighted by the
- *                       routing gates and added back into token order.
+ *                       routing gates and added back into token order;
+ *   pk_ring_attention -- one rank's share of ring attention: local queries against the key/value
+ *                       chunks of all ranks, merged through their log-sum-exp.
  *
  * Conventions shared by every entry point:
  *   - bf16 values are passed as uint16_t bit patterns (IEEE binary32 upper halves).
@@ -184,6 +186,34 @@ pk_status pk_grouped_combine(int64_t T, int top_k, int num_local,
 
 /* Device workspace bytes pk_grouped_combine needs (0 on invalid sizes). */
 size_t pk_grouped_combine_workspace_size(int num_local);
+
+/*
+ * pk_ring_attention -- one rank's share of ring attention ("Loads and Loads of Fluffy Kittens"
+ * summary, Key claims and Results: Ring Attention for sequence parallelism, B=16, D=128): the
+ * rank's queries attend to the key/value chunks of all ranks, one chunk after the other starting
+ * with `first_chunk`, and the per-chunk results are merged through their log-sum-exp.  The
+ * result is softmax attention over the concatenated keys (no mask):
+ *
+ *   O[b][i] = sum_j softmax_j(scale * Q[b][i] . K[b][j]) V[b][j],
+ *   lse[b][i] = log sum_j exp(scale * Q[b][i] . K[b][j])
+ *
+ * for every batch*head index b < BH and query row i < Sq, over the keys j of all chunks.
+ * Q: BH x Sq x D bf16, row i of b at Q + b*q_bh + i*ldq.  Chunk c: K_chunks[c], V_chunks[c],
+ * BH x chunk_len x D bf16 (b*k_bh + j*ldk, b*v_bh + j*ldv).  O: BH x Sq x D of o_dtype
+ * (b*o_bh + i*ldo); lse (optional, may be NULL): BH x Sq fp32 (b*lse_bh + i).  The softmax is
+ * carried in fp32 with the probabilities kept to ~16 significant bits.
+ * D must be 128; chunk_len a multiple of 64 (PK_ERR_UNSUPPORTED otherwise); 1 <= num_chunks <=
+ * PK_MAX_PARTS; 0 <= first_chunk < num_chunks; row strides % 8 == 0 (bf16) / 4 (fp32).
+ */
+pk_status pk_ring_attention(int64_t BH, int64_t Sq, int64_t D,
+                            const uint16_t* Q, int64_t q_bh, int64_t ldq,
+                            const uint16_t* const K_chunks[], const uint16_t* const V_chunks[],
+                            int num_chunks, int64_t chunk_len, int first_chunk,
+                            int64_t k_bh, int64_t ldk, int64_t v_bh, int64_t ldv,
+                            float scale,
+                            void* O, int64_t o_bh, int64_t ldo, pk_dtype o_dtype,
+                            float* lse, int64_t lse_bh,
+                            void* stream);
 
 /* Static description of a status code. */
 const char* pk_status_string(pk_status s);

@@ -91,7 +91,7 @@ def rs_prefill(M: int, N: int, partials: int, std: float, seed0: int,
 class Workload:
     """One synthetic workload: its kind, sizes and seeds (values only; no arithmetic)."""
     name: str
-    kind: str                  # "reduce" | "gemm" | "grouped" | "combine"
+    kind: str                  # "reduce" | "gemm" | "grouped" | "combine" | "attention"
     M: int = 0
     N: int = 0
     K: int = 0
@@ -119,6 +119,8 @@ class Workload:
     def flops(self) -> float:
         if self.kind in ("grouped", "combine"):
             raise ValueError("grouped flops depend on the routed row count")
+        if self.kind == "attention":  # QK^T and PV over all keys of all chunks
+            return 4.0 * self.M * self.N * self.chunks * self.tokens * self.K
         return 2.0 * self.M * self.N * self.K * self.producers
 
 
@@ -134,6 +136,9 @@ WORKLOADS: Dict[str, Workload] = {
                         prefill_std=0.02 * 0.02 * 32.0, prefill_seed=4011),
     "ar_16384": Workload("ar_16384", "reduce", M=16384, N=16384, K=2048, seed_a=5001,
                          seed_b=5002, producers=1, shards=1, cast_bf16=True),
+    "ring_attention": Workload("ring_attention", "attention", M=16 * 16, N=1024, K=128,
+                               std_a=1.0, std_b=1.0, seed_a=8001, seed_b=8101, chunks=8,
+                               tokens=1024),
     "moe_combine": Workload("moe_combine", "combine", K=2048, N=7168, std_a=1.0, std_b=0.02,
                             seed_a=7001, seed_b=7002, tokens=4096, top_k=8, num_experts=256,
                             num_local=32, expert_begin=0, zipf_s=1.1, seed_route=6003,
@@ -176,6 +181,16 @@ def combine_inputs(w: Workload):
     W = normal_bf16((w.num_local, w.K, w.N), w.std_b, w.seed_b)
     gates = topk_gates(w.tokens, w.top_k, w.seed_gates)
     return ids, H, W, gates
+
+
+def attention_inputs(w: Workload):
+    """Operands of the ring-attention local share: Q (BH x Sq x D) and the key / value chunks of
+    every rank (lists of BH x chunk x D), all ~N(0, 1) bf16.  M = BH, N = local queries,
+    K = head dimension, chunks = ranks, tokens = keys per chunk."""
+    Q = normal_bf16((w.M, w.N, w.K), w.std_a, w.seed_a)
+    Ks = [normal_bf16((w.M, w.tokens, w.K), w.std_a, w.seed_a + 1 + c) for c in range(w.chunks)]
+    Vs = [normal_bf16((w.M, w.tokens, w.K), w.std_b, w.seed_b + c) for c in range(w.chunks)]
+    return Q, Ks, Vs
 
 
 def describe() -> List[str]:

@@ -59,8 +59,9 @@ def bf16_ulp(x):
     return np.where(ax > 0, 2.0 ** (e - 7), 2.0 ** -133)
 
 
-def check_bf16(got_bits, ref, ref_rounded_bits, absprod=None, K=None, what=""):
-    """bf16 output vs binary64 reference R and its correctly rounded bits RNE(R)."""
+def check_bf16(got_bits, ref, ref_rounded_bits, absprod=None, K=None, what="", bound=None):
+    """bf16 output vs binary64 reference R and its correctly rounded bits RNE(R).  `bound` adds an
+    explicit per-element error bound of the computation before the final rounding."""
     got = bf16_bits_to_f64(got_bits)
     rr = bf16_bits_to_f64(ref_rounded_bits)
     relF, maxabs, rms = metrics(got, rr)
@@ -68,6 +69,8 @@ def check_bf16(got_bits, ref, ref_rounded_bits, absprod=None, K=None, what=""):
     slack = bf16_ulp(ref)
     if absprod is not None:
         slack = slack + gamma(K) * np.asarray(absprod)
+    if bound is not None:
+        slack = slack + np.asarray(bound)
     excess = np.abs(got - np.asarray(ref, np.float64)) - slack
     bad = np.argwhere(excess > 0)
     assert bad.size == 0, "%s: %d elements more than one bf16 ulp from R, first %s" % (

@@ -46,7 +46,11 @@ def test_rs_prefill_statistics():
 
 def test_workload_table():
     w = pk_inputs.WORKLOADS
-    assert set(w) == {"rs_tiny", "ag_8192", "rs_8192", "ar_16384", "moe_dispatch", "moe_combine"}
+    assert set(w) == {"rs_tiny", "ag_8192", "rs_8192", "ar_16384", "moe_dispatch", "moe_combine",
+                      "ring_attention"}
+    a = w["ring_attention"]
+    assert (a.M, a.N, a.K, a.chunks, a.tokens) == (256, 1024, 128, 8, 1024)
+    assert a.flops == 4.0 * 256 * 1024 * 8192 * 128
     # the combine returns the dispatch workload's routing: same routing table, D 2048 -> 7168
     c, d = w["moe_combine"], w["moe_dispatch"]
     assert (c.tokens, c.top_k, c.num_experts, c.num_local, c.zipf_s, c.seed_route) == \
