@@ -31,7 +31,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gemm_tile_granular_bf16_amd", "csrc", f)
-                  for f in ("pk_gemm.hip", "pk_internal.h")]
+                  for f in ("pk_gemm.hip", "pk_attention.hip", "pk_device.h", "pk_internal.h")]
 
 
 def kernel_source_hash() -> str:
@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="rs_8192",
                     choices=["rs_8192", "ag_8192", "ar_16384", "moe_dispatch", "moe_combine",
-                             "rs_tiny"])
+                             "ring_attention", "rs_tiny"])
     ap.add_argument("--mode", default="owner", choices=["owner", "atomic"])
     ap.add_argument("--no-variant", action="store_true", help="skip the other reduce mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -155,6 +155,23 @@ def setup_workload(name, mode, torch, pk):
         nbytes = 2 * (w.M * w.K + w.K * w.N + w.M * w.N)
         desc = {"M": w.M, "N": w.N, "K": w.K, "chunks": w.chunks, "out": "bf16"}
         return step, w.flops, nbytes, desc, (chunks, Bd, C)
+    if w.kind == "attention":
+        Q, Ks, Vs = pk_inputs.attention_inputs(w)
+        Qd = dev(Q)
+        Kd = [dev(k) for k in Ks]
+        Vd = [dev(v) for v in Vs]
+        del Q, Ks, Vs
+        O = torch.empty((w.M, w.N, w.K), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.M, w.N), device="cuda")
+
+        def step():
+            pk.ring_attention(Qd, Kd, Vd, O, lse, first_chunk=0)
+        keys = w.chunks * w.tokens
+        # Q, every key and value once, O and lse written once
+        nbytes = 2 * w.M * w.N * w.K * 2 + 2 * 2 * w.M * keys * w.K + 4 * w.M * w.N
+        desc = {"batch_heads": w.M, "local_queries": w.N, "head_dim": w.K, "chunks": w.chunks,
+                "keys_per_chunk": w.tokens, "out": "bf16"}
+        return step, w.flops, nbytes, desc, (Qd, Kd, Vd, O, lse)
     if w.kind == "combine":
         ids, H, W, gates = pk_inputs.combine_inputs(w)
         ids_d = torch.from_numpy(ids).cuda()
@@ -235,6 +252,26 @@ def cpu_baseline(name, target_s):
     w = pk_inputs.WORKLOADS[name]
     threads = oracle.default_threads()
     o = oracle.default()
+    if w.kind == "attention":
+        # the oracle on the first batch*head, for a growing prefix of its query rows
+        Q, Ks, Vs = pk_inputs.attention_inputs(w)
+        scale = 1.0 / np.sqrt(w.K)
+        K0, V0 = [k[0] for k in Ks], [v[0] for v in Vs]
+
+        def timed_a(n):
+            t = time.perf_counter()
+            o.ring_attention(np.ascontiguousarray(Q[0][:n]), K0, V0, scale, nthreads=threads)
+            return time.perf_counter() - t
+
+        n = 16
+        dt = timed_a(n)
+        if dt < target_s:
+            n = int(min(w.N, max(n, n * target_s / max(dt, 1e-3))))
+            dt = timed_a(n)
+        flops = 4.0 * n * w.chunks * w.tokens * w.K
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": "query rows 0..%d of batch*head 0 (of %d x %d), %d keys (%.1f s)"
+                          % (n - 1, w.M, w.N, w.chunks * w.tokens, dt)}
     if w.kind == "combine":
         # the oracle's dispatch, then its combine for a growing prefix of tokens
         ids, H, W, gates = pk_inputs.combine_inputs(w)
