@@ -384,6 +384,8 @@ pk_status pk_ring_attention(int64_t BH, int64_t Sq, int64_t D, const uint16_t* Q
         if (!aligned16(K_chunks[c]) || !aligned16(V_chunks[c]))
             return fail(PK_ERR_UNSUPPORTED, "chunk %d not 16-byte aligned", c);
     if (BH * ((Sq + 255) / 256) > INT32_MAX / 2) return fail(PK_ERR_UNSUPPORTED, "too many query tiles");
+    if (chunk_len / pk::ring_attention_block_keys() * num_chunks > INT32_MAX)
+        return fail(PK_ERR_UNSUPPORTED, "too many key blocks");
 
     pk::AttnArgs a{};
     a.BH = BH; a.Sq = Sq; a.chunk_len = chunk_len;

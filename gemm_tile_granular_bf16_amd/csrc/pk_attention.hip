@@ -14,8 +14,10 @@
 //
 // Kernel structure (one workgroup = 8 waves = 256 query rows of one (batch, head), 32 per wave):
 //  * the wave's Q block (32 x 128 bf16) stays in registers as MFMA operands for the whole pass;
-//  * key/value blocks of 64 rows go HBM -> LDS with direct 16-byte DMA, ST-stage pipeline, one
-//    barrier per block (the same protocol as the GEMM main loop);
+//  * key/value blocks of 64 rows go HBM -> LDS with direct 16-byte DMA, 3-stage pipeline, one
+//    barrier per block (the same protocol as the GEMM main loop).  The K tiles of all stages come
+//    first in LDS, then the V tiles, and the loop is unrolled by the stage count, so every LDS read
+//    is a per-lane base register plus a constant offset (no address arithmetic per block);
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the first operand, Q as the second)
 //    leaves every lane holding one query row, so the row max / row sum need only a swap with the
 //    lane 32 away (v_permlane32_swap) and the O rescale needs no cross-lane traffic at all;
@@ -26,8 +28,13 @@
 //    the probabilities to ~16 significant bits at the price of a second PV MFMA.
 //  * LDS rows are 256 bytes (128 bf16); the 16-byte chunk index is XORed with row % 16 for K
 //    (16 rows per read phase) and with 2 * (row % 8) for V (4 rows x 2 chunks per read phase).
+//  * The running max is raised lazily: only when a block's max exceeds it by more than 8 (log2
+//    units, a factor 2^8) in some row of the wave are O and l rescaled.  Softmax is invariant to the reference
+//    point, so this is the same function; the weights stay below 2^8, far from fp32 overflow.
 #include "pk_device.h"
 #include "pk_internal.h"
+
+#include <type_traits>
 
 namespace pk {
 
@@ -40,8 +47,9 @@ constexpr int kBM = kWaves * 32;         // query rows per workgroup
 constexpr int kBN = 64;                  // keys per block
 constexpr int kRowBytes = kD * 2;        // 256
 constexpr int kTileBytes = kBN * kRowBytes;   // 16 KB (K or V block)
-constexpr int kStageBytes = 2 * kTileBytes;   // K then V
 constexpr int kST = 3;                   // LDS stages
+constexpr int kVBase = kST * kTileBytes;      // V tiles after the K tiles of all stages
+constexpr float kLazyMax = 8.0f;         // raise the running max when exceeded by more than this
 constexpr int kLPS = 2 * (kTileBytes / 1024 / kWaves);  // DMA instructions per wave per block (4)
 
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
@@ -52,7 +60,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     const bf16x2 v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+// (a byte permute rather than a shift: the compiler would otherwise convert the fp32 value again)
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) {
+    return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu));
+}
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // table[i] for a wave-uniform i, with a chain of selects
@@ -74,7 +85,7 @@ __device__ __forceinline__ void partner_pair(float x, float& a, float& b) {
 }  // namespace
 
 __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p) {
-    __shared__ __attribute__((aligned(1024))) char lds[kST * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[2 * kST * kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -115,13 +126,17 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
         dma_ck[j] = pos ^ swz_k(row);  // global chunk this lane fetches into position pos
         dma_cv[j] = pos ^ swz_v(row);
     }
-    auto issue = [&](int64_t blk, int slot) {
-        const int64_t c = (p.first_chunk + blk / nb_chunk) % p.num_chunks;
-        const int64_t krow0 = (blk % nb_chunk) * kBN;
-        const uint16_t* kb = pick_attn(p.K, (int)c) + bh * p.k_bh + krow0 * p.ldk;
-        const uint16_t* vb = pick_attn(p.V, (int)c) + bh * p.v_bh + krow0 * p.ldv;
-        char* sk = lds + slot * kStageBytes;
-        char* sv = sk + kTileBytes;
+    // block numbers fit 32 bits (the host bounds them), and 32-bit division needs no branches
+    const uint32_t nbc32 = (uint32_t)nb_chunk;
+    auto issue = [&](int64_t blk, auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        const uint32_t bq = (uint32_t)blk / nbc32;
+        const int c = (int)(((uint32_t)p.first_chunk + bq) % (uint32_t)p.num_chunks);
+        const int64_t krow0 = (int64_t)((uint32_t)blk - bq * nbc32) * kBN;
+        const uint16_t* kb = pick_attn(p.K, c) + bh * p.k_bh + krow0 * p.ldk;
+        const uint16_t* vb = pick_attn(p.V, c) + bh * p.v_bh + krow0 * p.ldv;
+        char* sk = lds + slot * kTileBytes;
+        char* sv = lds + kVBase + slot * kTileBytes;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int b = j * kWaves + w;
@@ -131,29 +146,27 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
     };
 
     // ---- LDS read offsets ----------------------------------------------------------------------
-    // K operand of key block kb (32 keys), d-slice kk: row kb*32 + lane%32, chunk 2*kk + lane/32.
-    int k_off[2][kD / 16];
+    // K operand of key block kb (32 keys), d-slice kk: row kb*32 + lane%32, chunk 2*kk + lane/32;
+    // the swizzle sees the row only through lane%16, so key block kb is a constant offset
+    int k_off[kD / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + q32;
-#pragma unroll
-        for (int kk = 0; kk < kD / 16; ++kk)
-            k_off[kb][kk] = row * kRowBytes + (((2 * kk + h) ^ swz_k(row)) << 4);
-    }
+    for (int kk = 0; kk < kD / 16; ++kk)
+        k_off[kk] = q32 * kRowBytes + (((2 * kk + h) ^ swz_k(q32)) << 4);
     // V^T operand of d-block db, 16-key slice t: two transposing reads of 4 key rows each, rows
     // 16t + 4*(G/2) + (i/4) (lo) and 16t + 8 + 4*(G/2) + (i/4) (hi), columns
     // db*32 + 16*(G%2) + 4*(i%4) .. +3, for lane i of 16-lane group G.
+    // The swizzle of V sees the row only through row % 8, which 16t and +8 leave alone: one base
+    // per d-block, the slice and the lo/hi half are constant offsets.
     const int G = lane >> 4, i16 = lane & 15;
-    int v_lo_row[4], v_hi_row[4];
+    int v_off[kD / 32];
+    {
+        const int row = 4 * (G >> 1) + (i16 >> 2);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        v_lo_row[t] = 16 * t + 4 * (G >> 1) + (i16 >> 2);
-        v_hi_row[t] = v_lo_row[t] + 8;
+        for (int db = 0; db < kD / 32; ++db) {
+            const int d0 = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
+            v_off[db] = kVBase + row * kRowBytes + (((d0 >> 3) ^ swz_v(row)) << 4) + (d0 & 7) * 2;
+        }
     }
-    auto v_off = [&](int row, int db) {
-        const int d0 = db * 32 + 16 * (G & 1) + 4 * (i16 & 3);
-        return row * kRowBytes + ((((d0 >> 3)) ^ swz_v(row)) << 4) + (d0 & 7) * 2;
-    };
 
     // ---- running state -------------------------------------------------------------------------
     f32x16 oacc[kD / 32];
@@ -164,9 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
     float m_run = -INFINITY, l_run = 0.0f;
     const float sl2 = p.scale_log2;
 
-    auto process = [&](int slot) {
-        const char* sk = lds + slot * kStageBytes;
-        const char* sv = sk + kTileBytes;
+    auto process = [&](auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
         // S^T: lane = query, 16 keys per 32-key block
         f32x16 sacc[2];
 #pragma unroll
@@ -175,11 +187,12 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
             for (int kk = 0; kk < kD / 16; ++kk) {
-                const bf16x8 kf = *(const bf16x8*)(sk + k_off[kb][kk]);
+                const bf16x8 kf = *(const bf16x8*)(lds + slot * kTileBytes + kb * 32 * kRowBytes + k_off[kk]);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
             }
         }
-        // online softmax update (log2 units)
+        // online softmax (log2 units).  Scale first, then subtract: the strongest key of a row
+        // that sets the max gets exp2(+0) = 1 exactly.
         float mb = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -190,27 +203,30 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
             }
         float ma, mc;
         partner_pair(mb, ma, mc);
-        const float m_new = fmaxf(m_run, fmaxf(ma, mc));
-        // exp2 of an exact 0 is taken as exactly 1 (the hardware exp2 is only faithful): a block
-        // that does not raise the max leaves O and l untouched, and the maximal key weighs 1
-        const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        mb = fmaxf(ma, mc);
+        // raise the reference point only when the block exceeds it by more than kLazyMax in some
+        // row of the wave (always on the first block, where m_run = -inf)
+        if (__builtin_amdgcn_ballot_w64(mb > m_run + kLazyMax)) {
+            const float m_new = fmaxf(m_run, mb);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
         float rs = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float d = sacc[kb][r] - m_new;
-                sacc[kb][r] = d == 0.0f ? 1.0f : __builtin_amdgcn_exp2f(d);
+                sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r] - m_run);
                 rs += sacc[kb][r];
             }
         float ra, rc;
         partner_pair(rs, ra, rc);
-        l_run = l_run * alpha + (ra + rc);
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < kD / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        l_run += ra + rc;
         // P = hi + lo in bf16: per 16-key slice t, registers 8*(t%2) .. +7 of block t/2
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -218,18 +234,17 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float a = sacc[kb][r0 + 2 * e], b = sacc[kb][r0 + 2 * e + 1];
-                hi[e] = pack_bf16(a, b);
-                lo[e] = pack_bf16(a - bf16_lo_to_f32(hi[e]), b - bf16_hi_to_f32(hi[e]));
+                const float x = sacc[kb][r0 + 2 * e], y = sacc[kb][r0 + 2 * e + 1];
+                hi[e] = pack_bf16(x, y);
+                lo[e] = pack_bf16(x - bf16_lo_to_f32(hi[e]), y - bf16_hi_to_f32(hi[e]));
             }
             const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
             const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
 #pragma unroll
             for (int db = 0; db < kD / 32; ++db) {
-                const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    PK_LDS_PTR(i16x4, sv + v_off(v_lo_row[t], db)));
-                const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    PK_LDS_PTR(i16x4, sv + v_off(v_hi_row[t], db)));
+                const char* vp = lds + slot * kTileBytes + 16 * t * kRowBytes + v_off[db];
+                const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PK_LDS_PTR(i16x4, vp));
+                const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PK_LDS_PTR(i16x4, vp + 8 * kRowBytes));
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi, oacc[db], 0, 0, 0);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo, oacc[db], 0, 0, 0);
@@ -238,17 +253,25 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
     };
 
     // ---- pipeline over the key/value blocks (same protocol as the GEMM main loop) -------------
-#pragma unroll
-    for (int s = 0; s < kST - 1; ++s)
-        if (s < nb) issue(s, s);
-    for (int64_t blk = 0; blk < nb; ++blk) {
-        // block blk has landed (later blocks may still be in flight), and every wave is done
-        // with the slot about to be refilled
-        if (blk + 1 < nb && kST >= 3) wait_vmcnt<kLPS>(); else wait_vmcnt<0>();
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    static_assert(kST == 3, "the loop below is unrolled by the stage count");
+    if (0 < nb) issue(0, S0{});
+    if (1 < nb) issue(1, S1{});
+    // block blk in stage `slot` has landed (block blk+1 may still be in flight), and every wave is
+    // done with the stage about to be refilled, which held block blk-1
+    auto step = [&](int64_t blk, auto slot_c, auto refill_c) {
+        if (blk + 1 < nb) wait_vmcnt<kLPS>(); else wait_vmcnt<0>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        if (blk + kST - 1 < nb) issue(blk + kST - 1, (int)((blk + kST - 1) % kST));
-        process((int)(blk % kST));
+        if (blk + 2 < nb) issue(blk + 2, refill_c);
+        process(slot_c);
+    };
+    for (int64_t blk = 0; blk < nb; blk += kST) {
+        step(blk, S0{}, S2{});
+        if (blk + 1 < nb) step(blk + 1, S1{}, S0{});
+        if (blk + 2 < nb) step(blk + 2, S2{}, S1{});
     }
 
     // ---- output: O = O^T / l, lane = query row, 4 consecutive d per register group -------------
