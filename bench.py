@@ -165,12 +165,12 @@ def setup_workload(name, mode, torch, pk):
         lse = torch.empty((w.M, w.N), device="cuda")
 
         def step():
-            pk.ring_attention(Qd, Kd, Vd, O, lse, first_chunk=0)
+            pk.ring_attention(Qd, Kd, Vd, O, lse, first_chunk=0, probs="bf16")
         keys = w.chunks * w.tokens
         # Q, every key and value once, O and lse written once
         nbytes = 2 * w.M * w.N * w.K * 2 + 2 * 2 * w.M * keys * w.K + 4 * w.M * w.N
         desc = {"batch_heads": w.M, "local_queries": w.N, "head_dim": w.K, "chunks": w.chunks,
-                "keys_per_chunk": w.tokens, "out": "bf16"}
+                "keys_per_chunk": w.tokens, "out": "bf16", "probs": "bf16"}
         return step, w.flops, nbytes, desc, (Qd, Kd, Vd, O, lse)
     if w.kind == "combine":
         ids, H, W, gates = pk_inputs.combine_inputs(w)

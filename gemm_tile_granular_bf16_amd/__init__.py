@@ -19,12 +19,16 @@ import torch
 __all__ = [
     "PK_OK", "PK_ERR_INVALID_ARGUMENT", "PK_ERR_UNSUPPORTED", "PK_ERR_HIP", "PK_BF16", "PK_F32",
     "PK_REDUCE_ATOMIC", "PK_REDUCE_OWNER", "PK_MAX_PARTS", "PKError", "library", "library_path",
-    "gemm", "gemm_reduce", "grouped_gemm", "grouped_gemm_workspace_size",
+    "PK_PROBS_BF16", "PK_PROBS_SPLIT", "gemm", "gemm_reduce", "grouped_gemm",
+    "grouped_gemm_workspace_size", "grouped_combine", "grouped_combine_workspace_size",
+    "ring_attention",
 ]
 
 PK_OK, PK_ERR_INVALID_ARGUMENT, PK_ERR_UNSUPPORTED, PK_ERR_HIP = 0, 1, 2, 3
 PK_BF16, PK_F32 = 0, 1
 PK_REDUCE_ATOMIC, PK_REDUCE_OWNER = 0, 1
+PK_PROBS_BF16, PK_PROBS_SPLIT = 0, 1
+_PROBS = {"bf16": PK_PROBS_BF16, "split": PK_PROBS_SPLIT}
 PK_MAX_PARTS = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,7 +70,7 @@ def library() -> ctypes.CDLL:
     lib.pk_grouped_combine_workspace_size.argtypes = [i32]
     lib.pk_grouped_combine_workspace_size.restype = sz
     lib.pk_ring_attention.argtypes = [i64, i64, i64, p, i64, i64, p, p, i32, i64, i32, i64, i64,
-                                      i64, i64, ctypes.c_float, p, i64, i64, i32, p, i64, p]
+                                      i64, i64, ctypes.c_float, p, i64, i64, i32, p, i64, i32, p]
     lib.pk_ring_attention.restype = i32
     lib.pk_status_string.argtypes = [i32]
     lib.pk_status_string.restype = ctypes.c_char_p
@@ -178,12 +182,15 @@ def _bhsd(t: torch.Tensor, dtypes, what: str):
 
 def ring_attention(Q: torch.Tensor, K_chunks, V_chunks, O: torch.Tensor,
                    lse: Optional[torch.Tensor] = None, scale: Optional[float] = None,
-                   first_chunk: int = 0, stream=None):
+                   first_chunk: int = 0, probs: str = "bf16", stream=None):
     """One rank's share of ring attention (pk_ring_attention): ``Q`` (BH x Sq x 128 bf16)
     against the key/value chunks (lists of BH x chunk_len x 128 bf16, all the same length),
     visited from ``first_chunk`` on and merged through their log-sum-exp.  Writes ``O``
     (BH x Sq x 128, bf16 or fp32) and, if given, ``lse`` (BH x Sq fp32).  ``scale`` defaults to
-    1/sqrt(128)."""
+    1/sqrt(128).  ``probs``: "bf16" rounds the probabilities to bf16 before the product with V
+    (PK_PROBS_BF16), "split" carries them as two bf16 terms (PK_PROBS_SPLIT)."""
+    if probs not in _PROBS:
+        raise ValueError("probs must be one of %s" % sorted(_PROBS))
     qp, q_bh, ldq = _bhsd(Q, _BF16_LIKE, "Q")
     BH, Sq, D = Q.shape
     if len(K_chunks) != len(V_chunks) or not K_chunks:
@@ -218,7 +225,7 @@ def ring_attention(Q: torch.Tensor, K_chunks, V_chunks, O: torch.Tensor,
                                        ctypes.cast(Vp, ctypes.c_void_p), n, chunk_len, first_chunk,
                                        k_bh, ldk, v_bh, ldv, float(scale), op, o_bh, ldo,
                                        PK_BF16 if O.dtype == torch.bfloat16 else PK_F32, lp, lse_bh,
-                                       _stream_handle(stream)))
+                                       _PROBS[probs], _stream_handle(stream)))
     return O, lse
 
 

@@ -352,8 +352,9 @@ pk_status pk_ring_attention(int64_t BH, int64_t Sq, int64_t D, const uint16_t* Q
                             const uint16_t* const V_chunks[], int num_chunks, int64_t chunk_len,
                             int first_chunk, int64_t k_bh, int64_t ldk, int64_t v_bh, int64_t ldv,
                             float scale, void* O, int64_t o_bh, int64_t ldo, pk_dtype o_dtype,
-                            float* lse, int64_t lse_bh, void* stream) {
+                            float* lse, int64_t lse_bh, pk_attn_probs probs, void* stream) {
     if (BH < 0 || Sq < 0 || D < 0 || chunk_len < 0) return fail(PK_ERR_INVALID_ARGUMENT, "negative size");
+    if (probs != PK_PROBS_BF16 && probs != PK_PROBS_SPLIT) return fail(PK_ERR_INVALID_ARGUMENT, "probs");
     if (o_dtype != PK_BF16 && o_dtype != PK_F32) return fail(PK_ERR_INVALID_ARGUMENT, "o_dtype");
     if (num_chunks < 1 || num_chunks > PK_MAX_PARTS)
         return fail(PK_ERR_INVALID_ARGUMENT, "num_chunks %d outside 1..%d", num_chunks, PK_MAX_PARTS);
@@ -396,6 +397,7 @@ pk_status pk_ring_attention(int64_t BH, int64_t Sq, int64_t D, const uint16_t* Q
     a.scale_log2 = scale * 1.4426950408889634f;
     a.O = O; a.o_bh = o_bh; a.ldo = ldo; a.o_f32 = o_dtype == PK_F32;
     a.lse = lse; a.lse_bh = lse_bh;
+    a.split_probs = probs == PK_PROBS_SPLIT;
     return hip_status(pk::launch_ring_attention(a, (hipStream_t)stream), "pk_ring_attention launch");
 }
 

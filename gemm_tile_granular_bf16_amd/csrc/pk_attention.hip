@@ -22,12 +22,16 @@
 //    leaves every lane holding one query row, so the row max / row sum need only a swap with the
 //    lane 32 away (v_permlane32_swap) and the O rescale needs no cross-lane traffic at all;
 //  * O^T += V^T P^T: V^T comes from LDS with transposing reads (ds_read_b64_tr_b16), P from the
-//    S registers converted to bf16.  The MFMA k order is chosen to match the keys each lane
-//    already holds (4 + 4 keys per lane per 16-key slice), so P needs no shuffling: V^T's rows
-//    are read in the same order.  P is carried as the sum of two bf16 terms (hi + lo), which keeps
-//    the probabilities to ~16 significant bits at the price of a second PV MFMA.
+//    S registers converted to bf16 (round to nearest even), as the ThunderKittens attention step
+//    does before its PV product.  The MFMA k order is chosen to match the keys each lane already
+//    holds (4 + 4 keys per lane per 16-key slice), so P needs no shuffling: V^T's rows are read
+//    in the same order.  On request (SPLIT) P is carried as the sum of two bf16 terms (hi + lo),
+//    which keeps the probabilities to ~16 significant bits at the price of a second PV MFMA.
+//    The row sum l always adds the fp32 probabilities.
 //  * LDS rows are 256 bytes (128 bf16); the 16-byte chunk index is XORed with row % 16 for K
-//    (16 rows per read phase) and with 2 * (row % 8) for V (4 rows x 2 chunks per read phase).
+//    (16 rows per read phase) and with 4 * (row % 4) for V: a transposing read serves 32 lanes
+//    per phase, two 16-lane groups on the same 4 rows and different 16-column halves, and this
+//    swizzle spreads their 4 x 4 chunks over all 64 banks.
 //  * The running max is raised lazily: only when a block's max exceeds it by more than 8 (log2
 //    units, a factor 2^8) in some row of the wave are O and l rescaled.  Softmax is invariant to the reference
 //    point, so this is the same function; the weights stay below 2^8, far from fp32 overflow.
@@ -53,7 +57,7 @@ constexpr float kLazyMax = 8.0f;         // raise the running max when exceeded 
 constexpr int kLPS = 2 * (kTileBytes / 1024 / kWaves);  // DMA instructions per wave per block (4)
 
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 7) << 1; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
 
 // fp32 pair -> packed bf16 pair (round to nearest even, hardware convert)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -84,6 +88,7 @@ __device__ __forceinline__ void partner_pair(float x, float& a, float& b) {
 
 }  // namespace
 
+template <bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p) {
     __shared__ __attribute__((aligned(1024))) char lds[2 * kST * kTileBytes];
 
@@ -155,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
     // V^T operand of d-block db, 16-key slice t: two transposing reads of 4 key rows each, rows
     // 16t + 4*(G/2) + (i/4) (lo) and 16t + 8 + 4*(G/2) + (i/4) (hi), columns
     // db*32 + 16*(G%2) + 4*(i%4) .. +3, for lane i of 16-lane group G.
-    // The swizzle of V sees the row only through row % 8, which 16t and +8 leave alone: one base
+    // The swizzle of V sees the row only through row % 4, which 16t and +8 leave alone: one base
     // per d-block, the slice and the lo/hi half are constant offsets.
     const int G = lane >> 4, i16 = lane & 15;
     int v_off[kD / 32];
@@ -227,7 +232,8 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
         float ra, rc;
         partner_pair(rs, ra, rc);
         l_run += ra + rc;
-        // P = hi + lo in bf16: per 16-key slice t, registers 8*(t%2) .. +7 of block t/2
+        // P in bf16 (hi, plus lo = the rest when SPLIT): per 16-key slice t, registers
+        // 8*(t%2) .. +7 of block t/2
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int kb = t >> 1, r0 = 8 * (t & 1);
@@ -236,10 +242,10 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
             for (int e = 0; e < 4; ++e) {
                 const float x = sacc[kb][r0 + 2 * e], y = sacc[kb][r0 + 2 * e + 1];
                 hi[e] = pack_bf16(x, y);
-                lo[e] = pack_bf16(x - bf16_lo_to_f32(hi[e]), y - bf16_hi_to_f32(hi[e]));
+                if constexpr (SPLIT)
+                    lo[e] = pack_bf16(x - bf16_lo_to_f32(hi[e]), y - bf16_hi_to_f32(hi[e]));
             }
             const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
-            const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
 #pragma unroll
             for (int db = 0; db < kD / 32; ++db) {
                 const char* vp = lds + slot * kTileBytes + 16 * t * kRowBytes + v_off[db];
@@ -247,7 +253,10 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
                 const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PK_LDS_PTR(i16x4, vp + 8 * kRowBytes));
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi, oacc[db], 0, 0, 0);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo, oacc[db], 0, 0, 0);
+                if constexpr (SPLIT) {
+                    const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo, oacc[db], 0, 0, 0);
+                }
             }
         }
     };
@@ -308,7 +317,10 @@ hipError_t launch_ring_attention(const AttnArgs& a, hipStream_t stream) {
     const int64_t blocks = a.BH * n_qt;
     if (blocks <= 0) return hipSuccess;
     const int64_t grid = (blocks + 7) / 8 * 8;
-    hipLaunchKernelGGL(ring_attention_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    if (a.split_probs)
+        hipLaunchKernelGGL(ring_attention_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(ring_attention_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

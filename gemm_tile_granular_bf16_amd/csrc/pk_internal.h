@@ -118,6 +118,7 @@ struct AttnArgs {
     void* O;
     int64_t o_bh, ldo;
     int o_f32;
+    int split_probs;   // carry the probabilities as two bf16 terms (hi + lo)
     float* lse;        // may be null
     int64_t lse_bh;
 };

@@ -51,6 +51,11 @@ typedef enum pk_status {
     PK_ERR_HIP = 3               /* the HIP runtime rejected a launch */
 } pk_status;
 
+typedef enum pk_attn_probs {
+    PK_PROBS_BF16 = 0, /* attention probabilities rounded to bf16 before the PV product */
+    PK_PROBS_SPLIT = 1 /* carried as two bf16 terms, hi + lo (~16 significant bits) */
+} pk_attn_probs;
+
 typedef enum pk_dtype {
     PK_BF16 = 0, /* bf16, round to nearest even from the fp32 accumulator */
     PK_F32 = 1   /* the fp32 accumulator as is */
@@ -200,8 +205,10 @@ size_t pk_grouped_combine_workspace_size(int num_local);
  * for every batch*head index b < BH and query row i < Sq, over the keys j of all chunks.
  * Q: BH x Sq x D bf16, row i of b at Q + b*q_bh + i*ldq.  Chunk c: K_chunks[c], V_chunks[c],
  * BH x chunk_len x D bf16 (b*k_bh + j*ldk, b*v_bh + j*ldv).  O: BH x Sq x D of o_dtype
- * (b*o_bh + i*ldo); lse (optional, may be NULL): BH x Sq fp32 (b*lse_bh + i).  The softmax is
- * carried in fp32 with the probabilities kept to ~16 significant bits.
+ * (b*o_bh + i*ldo); lse (optional, may be NULL): BH x Sq fp32 (b*lse_bh + i).  Scores, the
+ * softmax and its row sums are fp32; the probabilities enter the product with V as bf16 (RNE),
+ * as in the ThunderKittens attention step (PK_PROBS_BF16), or, with PK_PROBS_SPLIT, as the sum of
+ * two bf16 terms (~16 significant bits, twice the matrix work of the PV product).
  * D must be 128; chunk_len a multiple of 64 (PK_ERR_UNSUPPORTED otherwise); 1 <= num_chunks <=
  * PK_MAX_PARTS; 0 <= first_chunk < num_chunks; row strides % 8 == 0 (bf16) / 4 (fp32).
  */
@@ -212,7 +219,7 @@ pk_status pk_ring_attention(int64_t BH, int64_t Sq, int64_t D,
                             int64_t k_bh, int64_t ldk, int64_t v_bh, int64_t ldv,
                             float scale,
                             void* O, int64_t o_bh, int64_t ldo, pk_dtype o_dtype,
-                            float* lse, int64_t lse_bh,
+                            float* lse, int64_t lse_bh, pk_attn_probs probs,
                             void* stream);
 
 /* Static description of a status code. */

@@ -37,11 +37,11 @@ def gamma(K):
     return ku / (1.0 - ku)
 
 
-def check_f32(got, ref, absprod=None, K=None, what=""):
+def check_f32(got, ref, absprod=None, K=None, what="", rel_tol=REL_F_TOL, maxabs_tol=MAXABS_RMS_TOL):
     """fp32 output vs binary64 reference: global tolerances + per-element sum bound."""
     relF, maxabs, rms = metrics(got, ref)
-    assert relF <= REL_F_TOL, "%s relF %.3e" % (what, relF)
-    assert maxabs <= MAXABS_RMS_TOL * rms or maxabs == 0.0, "%s maxabs %.3e rms %.3e" % (what, maxabs, rms)
+    assert relF <= rel_tol, "%s relF %.3e" % (what, relF)
+    assert maxabs <= maxabs_tol * rms or maxabs == 0.0, "%s maxabs %.3e rms %.3e" % (what, maxabs, rms)
     if absprod is not None:
         bound = gamma(K) * np.asarray(absprod) + 2.0 ** -24 * np.abs(ref) + 1e-30
         excess = np.abs(np.asarray(got, np.float64) - ref) - bound
@@ -59,13 +59,14 @@ def bf16_ulp(x):
     return np.where(ax > 0, 2.0 ** (e - 7), 2.0 ** -133)
 
 
-def check_bf16(got_bits, ref, ref_rounded_bits, absprod=None, K=None, what="", bound=None):
+def check_bf16(got_bits, ref, ref_rounded_bits, absprod=None, K=None, what="", bound=None,
+               rel_tol=REL_F_TOL):
     """bf16 output vs binary64 reference R and its correctly rounded bits RNE(R).  `bound` adds an
     explicit per-element error bound of the computation before the final rounding."""
     got = bf16_bits_to_f64(got_bits)
     rr = bf16_bits_to_f64(ref_rounded_bits)
     relF, maxabs, rms = metrics(got, rr)
-    assert relF <= REL_F_TOL, "%s relF vs RNE(R) %.3e" % (what, relF)
+    assert relF <= rel_tol, "%s relF vs RNE(R) %.3e" % (what, relF)
     slack = bf16_ulp(ref)
     if absprod is not None:
         slack = slack + gamma(K) * np.asarray(absprod)

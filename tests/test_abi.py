@@ -137,3 +137,31 @@ def test_combine_validation(lib):
     assert lib.pk_grouped_combine(*args(ldh=32)) == 1         # ldh < K
     assert lib.pk_grouped_combine(*args(K=60, ldh=64)) == 2   # K % 8
     assert lib.pk_grouped_combine(*args(ldo=66)) == 2         # ldo % 4
+
+
+@needs_no_gpu
+def test_ring_attention_validation(lib):
+    import math
+    t = _table(2)
+
+    def call(**kw):
+        a = dict(BH=2, Sq=64, D=128, ldq=128, n=2, L=64, first=0, ldk=128, ldv=128, scale=0.1,
+                 ldo=128, dt=0, probs=0)
+        a.update(kw)
+        return lib.pk_ring_attention(a["BH"], a["Sq"], a["D"], FAKE, a["Sq"] * a["ldq"], a["ldq"],
+                                     t, t, a["n"], a["L"], a["first"], a["L"] * a["ldk"], a["ldk"],
+                                     a["L"] * a["ldv"], a["ldv"], a["scale"], FAKE,
+                                     a["Sq"] * a["ldo"], a["ldo"], a["dt"], None, 0, a["probs"],
+                                     None)
+    assert call(Sq=0) == 0                     # nothing to do
+    assert call(BH=-1) == 1
+    assert call(probs=2) == 1                  # unknown probability mode
+    assert call(dt=5) == 1
+    assert call(n=0) == 1 and call(n=17) == 1
+    assert call(first=2) == 1
+    assert call(L=0) == 1                      # softmax over no keys
+    assert call(scale=math.nan) == 1
+    assert call(ldq=64) == 1                   # ld < D
+    assert call(D=64, ldq=64, ldk=64, ldv=64, ldo=64) == 2   # head dimension
+    assert call(L=96) == 2                     # chunk_len % 64
+    assert call(ldk=132) == 2                  # bf16 stride % 8
