@@ -30,26 +30,43 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "gemm_tile_granular_bf16_amd", "csrc", f)
-                  for f in ("pk_gemm.hip", "pk_attention.hip", "pk_device.h", "pk_internal.h")]
+# The sources each workload's dominant kernel is built from: a counter record stays valid until
+# one of them changes.
+KERNEL_SOURCES = {
+    "gemm": ("pk_gemm.hip", "pk_device.h", "pk_internal.h"),
+    "attention": ("pk_attention.hip", "pk_device.h", "pk_attention.h"),
+}
+WORKLOAD_TITLES = {
+    "rs_8192": "GEMM+RS local share N=8192",
+    "ag_8192": "AG+GEMM local share N=8192",
+    "ar_16384": "GEMM+AR local share N=16384",
+    "moe_dispatch": "token dispatch + expert GEMM (MoE local share)",
+    "moe_combine": "MoE combine (expert down-projection + gated scatter)",
+    "ring_attention": "ring attention local share B=16 H=16 D=128",
+    "rs_tiny": "GEMM+RS tiny (8 producers of 512x512x64)",
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_family(workload: str) -> str:
+    return "attention" if workload == "ring_attention" else "gemm"
+
+
+def kernel_source_hash(family: str = "gemm") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+    for f in KERNEL_SOURCES[family]:
+        h.update(open(os.path.join(ROOT, "gemm_tile_granular_bf16_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, mode: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on the
-    current kernel source (null otherwise)."""
+    current source of the workload's kernel (null otherwise)."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     rec = data.get("%s/%s" % (workload, mode))
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel_family(workload)):
         return None
     return rec.get("bytes_per_launch")
 
@@ -375,7 +392,7 @@ def main():
     roof["algorithmic_bytes"] = res["bytes"]
     roof["kernel_ms"] = round(res["kernel_ms"], 5)
     line = {
-        "metric": "TFLOP/s + % bf16 MFMA peak, GEMM+RS local share N=8192 (1 GPU)",
+        "metric": "TFLOP/s + % bf16 MFMA peak, " + WORKLOAD_TITLES[name] + " (1 GPU)",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -7,6 +7,7 @@
 
 #include <atomic>
 
+#include "pk_attention.h"
 #include "pk_internal.h"
 
 namespace {
