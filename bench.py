@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--mode", default="owner", choices=["owner", "atomic"])
     ap.add_argument("--no-variant", action="store_true", help="skip the other reduce mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true",
+                    help="skip the per-call, flushed and store-epilogue timings after the timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -158,6 +160,13 @@ def setup_workload(name, mode, torch, pk):
         desc = {"M": w.M, "N": w.N, "K": w.K, "producers": w.producers, "shards": w.shards,
                 "prefill_partials": w.prefill_partials, "reduce": mode,
                 "cast_bf16": w.cast_bf16}
+        if w.producers == 1:
+            # the same product with a plain store epilogue (bf16 C): the reference point for how
+            # much of the reduction stays exposed
+            a0, b0 = ops[0]
+            c_store = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+            desc["_gemm_only"] = lambda: pk.gemm(a0, b0, c_store)
+            return step, flops, nbytes, desc, (D, ops, out, c_store)
         return step, flops, nbytes, desc, (D, ops, out)
     if w.kind == "gemm":
         A = pk_inputs.normal_bf16((w.M, w.K), w.std_a, w.seed_a)
@@ -241,8 +250,64 @@ def setup_workload(name, mode, torch, pk):
     return step, flops, nbytes, desc, (ids_d, Xd, Wd, offsets, perm, Y, ws)
 
 
-def run_gpu(name, mode, steps, warmup, torch, pk):
+def per_call_ms(fn, torch, stream, calls, flush=None):
+    """Device time of each call between its own pair of events (outside the timed region);
+    `flush` runs before each call, outside the pair."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def detail_timing(step, gemm_only, torch, stream, calls):
+    """Median and mean per call, the same with L2 and the 256 MB memory-side cache flushed by a
+    512 MiB write before each call, and for a reduction the same product with a plain store
+    epilogue: (t_reduce - t_store) / t_reduce is the part of the reduction left exposed."""
+    warm = per_call_ms(step, torch, stream, calls)
+    scratch = torch.empty(128 << 20, device="cuda")  # 512 MiB
+    cold = per_call_ms(step, torch, stream, calls, flush=lambda: scratch.fill_(1.0))
+    del scratch
+    out = {"calls": calls, "median_ms": round(float(np.median(warm)), 5),
+           "mean_ms": round(float(np.mean(warm)), 5),
+           "flushed_median_ms": round(float(np.median(cold)), 5)}
+    if gemm_only is not None:
+        for _ in range(3):
+            gemm_only()
+        g = float(np.median(per_call_ms(gemm_only, torch, stream, calls)))
+        out["store_epilogue_median_ms"] = round(g, 5)
+        out["reduction_exposed_frac"] = round((out["median_ms"] - g) / out["median_ms"], 4)
+    return out
+
+
+def device_peak(torch):
+    """bf16 dense MFMA peak from the device: CUs x highest shader clock x 4096 flop/clk/CU (the
+    clock from the driver's DPM table; None where it cannot be read)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mhz = None
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            levels = [int(l.split(":")[1].strip().lower().replace("mhz", "").strip("* "))
+                      for l in open(f) if ":" in l]
+        except (OSError, ValueError, IndexError):
+            continue
+        if levels:
+            mhz = max(levels)
+            break
+    if mhz is None:
+        return {"cus": cus, "max_sclk_mhz": None, "tflops": None}
+    return {"cus": cus, "max_sclk_mhz": mhz, "tflops": round(cus * mhz * 1e6 * 4096 / 1e12, 1)}
+
+
+def run_gpu(name, mode, steps, warmup, torch, pk, detail=False):
     step, flops, nbytes, desc, keep = setup_workload(name, mode, torch, pk)
+    gemm_only = desc.pop("_gemm_only", None)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         step()
@@ -256,10 +321,21 @@ def run_gpu(name, mode, steps, warmup, torch, pk):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kms = timer.kernel_ms()
-    del keep
+    det = detail_timing(step, gemm_only, torch, stream, min(steps, 50)) if detail else None
+    del keep, gemm_only
     torch.cuda.empty_cache()
     return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kms, "flops": flops,
-            "bytes": nbytes, "desc": desc}
+            "bytes": nbytes, "desc": desc, "detail": det}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(name, target_s):
@@ -376,7 +452,7 @@ def main():
         calibrate_copy(torch)
         return
     name = args.workload
-    res = run_gpu(name, args.mode, args.steps, args.warmup, torch, pk)
+    res = run_gpu(name, args.mode, args.steps, args.warmup, torch, pk, detail=not args.no_detail)
     tflops = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
     ktflops = res["flops"] / (res["kernel_ms"] * 1e-3) / 1e12
     intensity = res["flops"] / res["bytes"]
@@ -408,6 +484,9 @@ def main():
         "config": dict({"workload": name}, **res["desc"]),
         "roofline": roof,
     }
+    if res["detail"] is not None:
+        line["timing"] = res["detail"]
+    line["peak_from_device"] = device_peak(torch)
     if name.startswith("rs") or name.startswith("ar"):
         if not args.no_variant:
             other = "atomic" if args.mode == "owner" else "owner"
@@ -418,6 +497,7 @@ def main():
     if not args.no_cpu_baseline:
         cb = cpu_baseline(name, args.cpu_seconds)
         if cb is not None:
+            cb["cpu_model"] = cpu_model()
             line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 

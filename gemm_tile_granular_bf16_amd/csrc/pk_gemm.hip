@@ -62,7 +62,7 @@ struct Cfg {
     static_assert(CPRB >= 16, "B swizzle needs at least 16 chunks per row");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 MFMA blocks");
     static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS is 160 KB per CU");
-    static_assert(ST >= 2 && ST <= 3, "pipeline depth");
+    static_assert(ST >= 2 && ST <= 5, "pipeline depth");
 };
 
 using Cfg256x256 = Cfg<256, 256, 64, 2, 4, 2>;     // 8 waves of 128x64, 128 KB LDS
@@ -319,17 +319,23 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
     auto stage_in = [&](int64_t j, int slot) {
         if (tail_here && j == nkl - 1) issue_tail(kt_begin + j, slot); else issue(kt_begin + j, slot);
     };
+    // Wait until the oldest step in flight has landed while `later` (clamped to ST-2) younger
+    // steps may stay in flight: each full step is LPS loads per wave, counted in issue order.  A
+    // ragged step is loaded through registers and waited for when it is issued, which drains
+    // every older load too, so no count is too small once it has been issued.
+    auto wait_oldest = [&](int64_t later) {
+        if constexpr (C::ST >= 5) if (later >= 3) { wait_vmcnt<3 * C::LPS>(); return; }
+        if constexpr (C::ST >= 4) if (later >= 2) { wait_vmcnt<2 * C::LPS>(); return; }
+        if constexpr (C::ST >= 3) if (later >= 1) { wait_vmcnt<C::LPS>(); return; }
+        wait_vmcnt<0>();
+    };
     if (nkl > 0) {
         // prologue: steps 0 .. ST-2 in flight, wait for step 0, then refill with step ST-1
 #pragma unroll
         for (int st = 0; st < C::ST - 1; ++st)
             if (st < nkl) stage_in(st, st);
         wait_lgkmcnt0();
-        if constexpr (C::ST >= 3) {
-            if (nkl >= 2) wait_vmcnt<C::LPS * (C::ST - 2)>(); else wait_vmcnt<0>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        wait_oldest(nkl - 1);
         __builtin_amdgcn_s_barrier();
         if (C::ST - 1 < nkl) stage_in(C::ST - 1, C::ST - 1);
         bf16x8 fa[2][C::FM], fb[2][C::FN];
@@ -360,12 +366,9 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
                     }
                 } else if constexpr (MODE != MODE_LAST) {
                     wait_lgkmcnt0();
-                    if constexpr (C::ST >= 3) {
-                        // a later step than j+1 is in flight unless j+1 is the last one
-                        if (MODE != MODE_DRAIN || j + 2 < nkl) wait_vmcnt<C::LPS>(); else wait_vmcnt<0>();
-                    } else {
-                        wait_vmcnt<0>();
-                    }
+                    // steps j+2 .. j+ST-1 may stay in flight (fewer near the end)
+                    if constexpr (MODE != MODE_DRAIN) wait_vmcnt<C::LPS * (C::ST - 2)>();
+                    else wait_oldest(nkl - 2 - j);
                     __builtin_amdgcn_s_barrier();
                     if constexpr (MODE == MODE_ISSUE) issue(kt_begin + j + C::ST, slot);
                     if constexpr (MODE == MODE_TAIL) issue_tail(kt_begin + j + C::ST, slot);
