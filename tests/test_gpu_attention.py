@@ -174,3 +174,44 @@ def test_attention_local_share_workload_sampled(pk, oracle_mod):
             check_bf16(Ob[b][rows], R, o.round_bf16(R), what="ring %s b=%d" % (probs, b),
                        bound=g["eps"] * wb + 1e-7, rel_tol=g["rel"])
             assert np.max(np.abs(L[b][rows] - Rl)) <= 1e-4
+
+
+def test_attention_single_query_sixteen_chunks_from_the_last(pk, oracle_mod):
+    """One query row per (batch, head), the most chunks a call takes (16 of 64 keys), visited
+    from the last one; fp32 output against the oracle, both probability modes."""
+    BH, Sq, n, Lc = 5, 1, 16, 64
+    Q, K, V = _inputs(BH, Sq, n, Lc, 341)
+    scale = 1.0 / np.sqrt(D)
+    for probs in sorted(MODES):
+        O, lse = _run(pk, Q, K, V, scale, first=n - 1, probs=probs)
+        _check(oracle_mod.default(), Q, K, V, scale, O, lse, what="Sq=1 " + probs, probs=probs)
+
+
+def test_attention_padded_rows_and_empty_queries(pk, oracle_mod):
+    """Row strides beyond the head dimension (Q, K, V and an fp32 O inside wider buffers, and a
+    batch*head stride with a gap): only the addressed elements are read and written.  No query
+    rows: the call returns without touching O."""
+    BH, Sq, n, Lc = 2, 96, 3, 128
+    Q, K, V = _inputs(BH, Sq, n, Lc, 351)
+    scale = 0.09
+
+    def padded(bits, width, extra_rows=0):
+        b, s, _ = bits.shape
+        full = np.zeros((b, s + extra_rows, width), dtype=np.uint16)
+        full[:, :s, :D] = bits
+        return dev_bf16(full)[:, :s, :D]
+
+    Qd = padded(Q, 136, extra_rows=5)
+    Kd = [padded(k, 192) for k in K]
+    Vd = [padded(v, 144, extra_rows=3) for v in V]
+    Ofull = torch.full((BH, Sq, 140), 7.0, device="cuda")
+    O = Ofull[:, :, :D]
+    lse = torch.full((BH, Sq), float("nan"), device="cuda")
+    pk.ring_attention(Qd, Kd, Vd, O, lse, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.all(Ofull[:, :, D:] == 7.0)   # the padding is never written
+    _check(oracle_mod.default(), Q, K, V, scale, O, lse, what="padded")
+    # no query rows: nothing happens
+    Oe = torch.full((BH, 0, D), 1.0, device="cuda")
+    pk.ring_attention(Qd[:, :0], Kd, Vd, Oe, scale=scale)
+    torch.cuda.synchronize()
