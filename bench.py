@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -51,10 +52,18 @@ def kernel_family(workload: str) -> str:
     return "attention" if workload == "ring_attention" else "gemm"
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(family: str = "gemm") -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
-        h.update(open(os.path.join(ROOT, "gemm_tile_granular_bf16_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "gemm_tile_granular_bf16_amd", "csrc", f)).read()
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -33,8 +33,9 @@
 //    per phase, two 16-lane groups on the same 4 rows and different 16-column halves, and this
 //    swizzle spreads their 4 x 4 chunks over all 64 banks.
 //  * The running max is raised lazily: only when a block's max exceeds it by more than 8 (log2
-//    units, a factor 2^8) in some row of the wave are O and l rescaled.  Softmax is invariant to the reference
-//    point, so this is the same function; the weights stay below 2^8, far from fp32 overflow.
+//    units, a factor 2^8) in some row of the wave are O and l rescaled.  Softmax is invariant to
+//    the reference point, so this is the same function; the weights stay below 2^8, far from
+//    fp32 overflow.
 #include "pk_attention.h"
 #include "pk_device.h"
 

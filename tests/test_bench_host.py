@@ -47,3 +47,10 @@ def test_traffic_records_are_keyed_to_their_kernel_source(tmp_path, monkeypatch)
     assert bench.measured_traffic("rs_8192", "owner") == 123
     assert bench.measured_traffic("ring_attention", "owner") is None   # stale source
     assert bench.measured_traffic("ag_8192", "owner") is None          # no record
+
+
+def test_source_hash_ignores_comments_and_layout():
+    a = "int f(int x) {  // doubles\n    return 2 * x; /* no overflow check */\n}\n"
+    b = "int f(int x) {\n return 2 * x;\n}"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(a.replace("2 * x", "3 * x"))
