@@ -95,9 +95,48 @@ def parse():
                     help="skip the per-call, flushed and store-epilogue timings after the timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the pages' N sweep of the AG and RS local shares (context, several lines)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def sweep(torch, pk, calls):
+    """The pages' shape sweep as context (not the headline): the GEMM+RS local share
+    N x N x N/8 (owner and atomic reduction into 8 row shards of an fp32 destination) and the
+    AG+GEMM local share N x N/8 x N (A as 8 row-chunks, bf16 output), for N = 2048 .. 16384.
+    Inputs are seeded normals drawn on the device; one JSON line per point, median per call."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9001)
+    rnd = lambda r, c: (torch.randn(r, c, generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    for n in (2048, 4096, 8192, 16384):
+        k = n // 8
+        A, B = rnd(n, k), rnd(k, n)
+        D = torch.zeros(n, n, device="cuda")
+        shards = list(D.split(n // 8))
+        flops = 2.0 * n * n * k
+        for mode, mid in (("owner", pk.PK_REDUCE_OWNER), ("atomic", pk.PK_REDUCE_ATOMIC)):
+            fn = lambda: pk.gemm_reduce(A, B, shards, mode=mid)
+            for _ in range(3):
+                fn()
+            ms = float(np.median(per_call_ms(fn, torch, stream, calls)))
+            print(json.dumps({"sweep": "gemm_rs", "N": n, "reduce": mode, "M": n, "N_cols": n, "K": k,
+                              "median_ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1)}), flush=True)
+        del A, B, D, shards
+        A = rnd(n, n)
+        chunks = list(A.split(n // 8))
+        B = rnd(n, k)
+        C = torch.empty(n, k, dtype=torch.bfloat16, device="cuda")
+        fn = lambda: pk.gemm(chunks, B, C)
+        for _ in range(3):
+            fn()
+        ms = float(np.median(per_call_ms(fn, torch, stream, calls)))
+        print(json.dumps({"sweep": "ag_gemm", "N": n, "M": n, "N_cols": k, "K": n,
+                          "median_ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1)}), flush=True)
+        del A, chunks, B, C
+        torch.cuda.empty_cache()
 
 
 def calibrate_copy(torch):
@@ -459,6 +498,9 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.sweep:
+        sweep(torch, pk, max(args.steps, 10))
         return
     name = args.workload
     res = run_gpu(name, args.mode, args.steps, args.warmup, torch, pk, detail=not args.no_detail)
