@@ -14,8 +14,10 @@
 //
 // Kernel structure (one workgroup = 8 waves = 256 query rows of one (batch, head), 32 per wave):
 //  * the wave's Q block (32 x 128 bf16) stays in registers as MFMA operands for the whole pass;
-//  * key/value blocks of 64 rows go HBM -> LDS with direct 16-byte DMA, 3-stage pipeline, one
-//    barrier per block (the same protocol as the GEMM main loop).  The K tiles of all stages come
+//  * key/value blocks of 128 rows (2 LDS stages), or of 64 rows (3 stages) when the chunk length
+//    is not a multiple of 128, go HBM -> LDS with direct 16-byte DMA, one barrier per block (the
+//    same protocol as the GEMM main loop); the longer block halves the barriers and the max
+//    updates per key.  The K tiles of all stages come
 //    first in LDS, then the V tiles, and the loop is unrolled by the stage count, so every LDS read
 //    is a per-lane base register plus a constant offset (no address arithmetic per block);
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the first operand, Q as the second)
@@ -49,13 +51,23 @@ constexpr int kD = 128;                  // head dimension
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kWaves * 32;         // query rows per workgroup
-constexpr int kBN = 64;                  // keys per block
 constexpr int kRowBytes = kD * 2;        // 256
-constexpr int kTileBytes = kBN * kRowBytes;   // 16 KB (K or V block)
-constexpr int kST = 3;                   // LDS stages
-constexpr int kVBase = kST * kTileBytes;      // V tiles after the K tiles of all stages
 constexpr float kLazyMax = 8.0f;         // raise the running max when exceeded by more than this
-constexpr int kLPS = 2 * (kTileBytes / 1024 / kWaves);  // DMA instructions per wave per block (4)
+constexpr int kMinBN = 64;               // chunk lengths are multiples of this
+
+// Key-block geometry: BN keys per block, K and V tiles of BN rows, ST LDS stages.
+template <int BN>
+struct Blocks {
+    static constexpr int kBN = BN;
+    static constexpr int kTileBytes = BN * kRowBytes;            // K or V tile
+    static constexpr int kST = BN == 64 ? 3 : 2;                  // LDS stages (96 / 128 KB)
+    static constexpr int kVBase = kST * kTileBytes;               // V tiles after the K tiles
+    static constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // 1 KB DMA blocks per wave
+    static constexpr int kLPS = 2 * kDmaPerWave;                  // DMA instructions per block
+    static constexpr int kKB = BN / 32;                           // 32-key MFMA blocks
+    static constexpr int kSlices = BN / 16;                       // 16-key slices of P
+    static_assert(BN == 64 || BN == 128, "key block");
+};
 
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
@@ -89,8 +101,12 @@ __device__ __forceinline__ void partner_pair(float x, float& a, float& b) {
 
 }  // namespace
 
-template <bool SPLIT>
+template <bool SPLIT, int BN>
 __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p) {
+    using Bk = Blocks<BN>;
+    constexpr int kBN = Bk::kBN, kTileBytes = Bk::kTileBytes, kST = Bk::kST, kVBase = Bk::kVBase;
+    constexpr int kDmaPerWave = Bk::kDmaPerWave, kLPS = Bk::kLPS, kKB = Bk::kKB;
+    constexpr int kSlices = Bk::kSlices;
     __shared__ __attribute__((aligned(1024))) char lds[2 * kST * kTileBytes];
 
     const int tid = threadIdx.x;
@@ -120,11 +136,11 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
     // ---- key/value block schedule ------------------------------------------------------------
     const int64_t nb_chunk = p.chunk_len / kBN;
     const int64_t nb = nb_chunk * p.num_chunks;
-    // DMA: K (and V) block = 16 KB = 16 one-KB blocks; wave w moves blocks w and w + 8; lane i
+    // DMA: a K (and V) tile is made of 1 KB blocks; wave w moves blocks w, w + 8, ...; lane i
     // fills LDS row 4*b + i/16, 16-byte position i%16.
-    int dma_row[2], dma_ck[2], dma_cv[2];
+    int dma_row[kDmaPerWave], dma_ck[kDmaPerWave], dma_cv[kDmaPerWave];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kDmaPerWave; ++j) {
         const int b = j * kWaves + w;
         const int row = 4 * b + (lane >> 4);
         const int pos = lane & 15;
@@ -144,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
         char* sk = lds + slot * kTileBytes;
         char* sv = lds + kVBase + slot * kTileBytes;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < kDmaPerWave; ++j) {
             const int b = j * kWaves + w;
             dma16(kb + (int64_t)dma_row[j] * p.ldk + dma_ck[j] * 8, sk + b * 1024);
             dma16(vb + (int64_t)dma_row[j] * p.ldv + dma_cv[j] * 8, sv + b * 1024);
@@ -186,9 +202,9 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
     auto process = [&](auto slot_c) {
         constexpr int slot = decltype(slot_c)::value;
         // S^T: lane = query, 16 keys per 32-key block
-        f32x16 sacc[2];
+        f32x16 sacc[kKB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
@@ -201,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
         // that sets the max gets exp2(+0) = 1 exactly.
         float mb = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 sacc[kb][r] *= sl2;
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
         }
         float rs = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r] - m_run);
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
         // P in bf16 (hi, plus lo = the rest when SPLIT): per 16-key slice t, registers
         // 8*(t%2) .. +7 of block t/2
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < kSlices; ++t) {
             const int kb = t >> 1, r0 = 8 * (t & 1);
             uint32_t hi[4], lo[4];
 #pragma unroll
@@ -263,25 +279,39 @@ __global__ __launch_bounds__(kThreads, 1) void ring_attention_kernel(AttnArgs p)
     };
 
     // ---- pipeline over the key/value blocks (same protocol as the GEMM main loop) -------------
+    // Step blk: block blk has landed (with 3 stages block blk+1 may still be in flight), every
+    // wave is done with the stage about to be refilled (it held block blk-1), the refill goes
+    // out, then the block is processed.  The loop is unrolled by the stage count.
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
-    static_assert(kST == 3, "the loop below is unrolled by the stage count");
-    if (0 < nb) issue(0, S0{});
-    if (1 < nb) issue(1, S1{});
-    // block blk in stage `slot` has landed (block blk+1 may still be in flight), and every wave is
-    // done with the stage about to be refilled, which held block blk-1
+    for (int s = 0; s < kST - 1; ++s)
+        if (s < nb) {
+            if (s == 0) issue(0, S0{}); else issue(1, S1{});
+        }
     auto step = [&](int64_t blk, auto slot_c, auto refill_c) {
-        if (blk + 1 < nb) wait_vmcnt<kLPS>(); else wait_vmcnt<0>();
+        if constexpr (kST == 3) {
+            if (blk + 1 < nb) wait_vmcnt<kLPS>(); else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        if (blk + 2 < nb) issue(blk + 2, refill_c);
+        if (blk + kST - 1 < nb) issue(blk + kST - 1, refill_c);
         process(slot_c);
     };
-    for (int64_t blk = 0; blk < nb; blk += kST) {
-        step(blk, S0{}, S2{});
-        if (blk + 1 < nb) step(blk + 1, S1{}, S0{});
-        if (blk + 2 < nb) step(blk + 2, S2{}, S1{});
+    if constexpr (kST == 3) {
+        for (int64_t blk = 0; blk < nb; blk += 3) {
+            step(blk, S0{}, S2{});
+            if (blk + 1 < nb) step(blk + 1, S1{}, S0{});
+            if (blk + 2 < nb) step(blk + 2, S2{}, S1{});
+        }
+    } else {
+        static_assert(kST == 2, "2 or 3 stages");
+        for (int64_t blk = 0; blk < nb; blk += 2) {
+            step(blk, S0{}, S1{});
+            if (blk + 1 < nb) step(blk + 1, S1{}, S0{});
+        }
     }
 
     // ---- output: O = O^T / l, lane = query row, 4 consecutive d per register group -------------
@@ -318,14 +348,19 @@ hipError_t launch_ring_attention(const AttnArgs& a, hipStream_t stream) {
     const int64_t blocks = a.BH * n_qt;
     if (blocks <= 0) return hipSuccess;
     const int64_t grid = (blocks + 7) / 8 * 8;
-    if (a.split_probs)
-        hipLaunchKernelGGL(ring_attention_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(ring_attention_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    const dim3 g((unsigned)grid), b(kThreads);
+    const bool long_blocks = a.chunk_len % 128 == 0;
+    if (a.split_probs) {
+        if (long_blocks) hipLaunchKernelGGL((ring_attention_kernel<true, 128>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((ring_attention_kernel<true, 64>), g, b, 0, stream, a);
+    } else {
+        if (long_blocks) hipLaunchKernelGGL((ring_attention_kernel<false, 128>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((ring_attention_kernel<false, 64>), g, b, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
-int ring_attention_block_keys() { return kBN; }
+int ring_attention_block_keys() { return kMinBN; }
 int ring_attention_head_dim() { return kD; }
 
 }  // namespace pk
