@@ -91,6 +91,8 @@ def parse():
     ap.add_argument("--mode", default="owner", choices=["owner", "atomic"])
     ap.add_argument("--no-variant", action="store_true", help="skip the other reduce mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying a captured HIP graph")
     ap.add_argument("--no-detail", action="store_true",
                     help="skip the per-call, flushed and store-epilogue timings after the timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -166,9 +168,9 @@ class Timer:
     def begin(self):
         self.start.record(self.stream)
 
-    def step(self, fn):
+    def step(self, fn, count=1):
         fn()
-        self.steps += 1
+        self.steps += count
 
     def finish(self):
         self.end.record(self.stream)
@@ -353,27 +355,76 @@ def device_peak(torch):
     return {"cus": cus, "max_sclk_mhz": mhz, "tflops": round(cus * mhz * 1e6 * 4096 / 1e12, 1)}
 
 
-def run_gpu(name, mode, steps, warmup, torch, pk, detail=False):
+# Workloads whose step is replayed from a captured HIP graph: their kernels allocate nothing,
+# clear nothing with memset nodes and give the same bits on every replay (tests/test_gpu_graph.py).
+# The grouped workloads (dispatch counters, split-tail partial sums) run eagerly.
+GRAPH_KINDS = ("reduce", "gemm", "attention")
+
+
+def graph_batch(steps: int) -> int:
+    """Steps per captured graph: the largest divisor of `steps` up to 10."""
+    if steps < 1:
+        return 1
+    return max(d for d in range(1, min(steps, 10) + 1) if steps % d == 0)
+
+
+def capture_steps(step, per, torch):
+    """`per` steps captured into one graph on a side stream (the stream the binding sees as
+    current while capturing)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(per):
+            step()
+    torch.cuda.synchronize()
+    return g
+
+
+def wall_ms_per_step(fn, steps, torch):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def run_gpu(name, mode, steps, warmup, torch, pk, detail=False, graph=False):
+    import pk_inputs
     step, flops, nbytes, desc, keep = setup_workload(name, mode, torch, pk)
     gemm_only = desc.pop("_gemm_only", None)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    graph = graph and pk_inputs.WORKLOADS[name].kind in GRAPH_KINDS
+    eager_ms, g, per = None, None, 1
+    if graph:
+        eager_ms = wall_ms_per_step(step, min(steps, 20), torch)
+        per = graph_batch(steps)
+        g = capture_steps(step, per, torch)
+        g.replay()  # untimed
+        torch.cuda.synchronize()
+    desc["launch"] = "hip graph of %d steps" % per if graph else "eager"
     timer = Timer(torch, stream)
     t0 = time.perf_counter()
     timer.begin()
-    for _ in range(steps):
-        timer.step(step)
+    if graph:
+        for _ in range(steps // per):
+            timer.step(g.replay, per)
+    else:
+        for _ in range(steps):
+            timer.step(step)
     timer.finish()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kms = timer.kernel_ms()
     det = detail_timing(step, gemm_only, torch, stream, min(steps, 50)) if detail else None
-    del keep, gemm_only
+    del keep, gemm_only, g
     torch.cuda.empty_cache()
     return {"ms_per_step": wall * 1e3 / steps, "kernel_ms": kms, "flops": flops,
-            "bytes": nbytes, "desc": desc, "detail": det}
+            "bytes": nbytes, "desc": desc, "detail": det, "eager_ms_per_step": eager_ms}
 
 
 def cpu_model():
@@ -503,7 +554,8 @@ def main():
         sweep(torch, pk, max(args.steps, 10))
         return
     name = args.workload
-    res = run_gpu(name, args.mode, args.steps, args.warmup, torch, pk, detail=not args.no_detail)
+    res = run_gpu(name, args.mode, args.steps, args.warmup, torch, pk, detail=not args.no_detail,
+                  graph=not args.eager)
     tflops = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
     ktflops = res["flops"] / (res["kernel_ms"] * 1e-3) / 1e12
     intensity = res["flops"] / res["bytes"]
@@ -537,6 +589,8 @@ def main():
     }
     if res["detail"] is not None:
         line["timing"] = res["detail"]
+    if res["eager_ms_per_step"] is not None:
+        line["eager_ms_per_step"] = round(res["eager_ms_per_step"], 5)
     line["peak_from_device"] = device_peak(torch)
     if name.startswith("rs") or name.startswith("ar"):
         if not args.no_variant:
