@@ -143,6 +143,33 @@ def test_ragged_shards_with_bf16_output(pk, oracle_mod, mode):
     assert np.all(out[:, N:] == 0x40e0)  # bf16 bits of 7.0
 
 
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_large_ragged_with_straddling_shards(pk, oracle_mod, mode):
+    """More 256x256 tiles (17 x 33) than the device runs workgroups at once, ragged in every
+    dimension, shards of 544 rows (128-row bands of the owner epilogue straddle shard
+    boundaries, which takes its per-row shard path), padded leading dimensions and the bf16
+    output."""
+    M, N, K = 4200, 8200, 72
+    log("pk_gemm_reduce large ragged M=%d N=%d K=%d mode=%d" % (M, N, K, mode))
+    A = pk_inputs.normal_bf16((M, K), 1.0, 131)
+    B = pk_inputs.normal_bf16((K, N), 1.0, 132)
+    D0 = np.random.Generator(np.random.PCG64(133)).standard_normal((M, N)).astype(np.float32)
+    base = torch.zeros((M, N + 24), device="cuda")
+    base[:, :N] = torch.from_numpy(D0).cuda()
+    base[:, N:] = 5.0
+    shards = [base[r:r + 544, :N] for r in range(0, M, 544)]
+    out_base = torch.full((M, N + 8), 7.0, dtype=torch.bfloat16, device="cuda")
+    pk.gemm_reduce(dev_bf16(A), dev_bf16(B), shards, mode=mode, out_bf16=out_base[:, :N])
+    torch.cuda.synchronize()
+    got = host_f32(base)
+    assert np.all(got[:, N:] == 5.0)
+    R = oracle_mod.reduce(D0, [(A, B)])
+    _check_reduce(got[:, :N], R, [(A, B)], D0, "large ragged")
+    out = host_bits(out_base)
+    assert np.array_equal(out[:, :N], oracle_mod.cast_f32_bf16(np.ascontiguousarray(got[:, :N])))
+    assert np.all(out[:, N:] == 0x40e0)
+
+
 def test_k_zero_adds_nothing_and_cast_still_runs(pk, oracle_mod):
     M, N = 96, 64
     D0 = np.random.Generator(np.random.PCG64(7)).standard_normal((M, N)).astype(np.float32)
