@@ -57,10 +57,13 @@ def test_integer_producers_bit_exact(pk, oracle_mod, mode):
               pk_inputs.small_int_bf16((K, N), -3, 3, 400 + p)) for p in range(8)]
     D0 = np.random.Generator(np.random.PCG64(9)).integers(-100, 100, size=(M, N)).astype(np.float32)
     D = torch.from_numpy(D0).cuda()
+    # every producer's operands uploaded and kept alive before any launch: a temporary freed
+    # while its kernel waits on another stream would be reused by the next upload
+    dev = [(dev_bf16(a), dev_bf16(b)) for a, b in prods]
     streams = [torch.cuda.Stream() for _ in prods] if mode == 0 else [None] * len(prods)
     torch.cuda.synchronize()
-    for s, (a, b) in zip(streams, prods):
-        pk.gemm_reduce(dev_bf16(a), dev_bf16(b), D, mode=mode, stream=s)
+    for s, (a, b) in zip(streams, dev):
+        pk.gemm_reduce(a, b, D, mode=mode, stream=s)
     torch.cuda.synchronize()
     assert np.array_equal(host_f32(D).astype(np.float64), oracle_mod.reduce(D0, prods))
 
