@@ -78,6 +78,13 @@ pk::TileCfgId pick_store_cfg(int64_t M, int64_t N) {
 // Tile shape for the reduction epilogues: the same rule as the stores.
 pk::TileCfgId pick_reduce_cfg(int64_t M, int64_t N) { return pick_store_cfg(M, N); }
 
+// The 256x256 tile stages k-steps through registers when every k-step is whole (measured faster
+// than direct-to-LDS loads on the 8192^2 x 1024 and 16384^2 x 2048 shares); a ragged last k-step
+// keeps the direct-to-LDS loop, which zero-fills it.
+pk::TileCfgId with_staging(pk::TileCfgId cfg, int64_t K) {
+    return cfg == pk::CFG_256x256 && K % 64 == 0 ? pk::CFG_256x256R : cfg;
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,7 +149,7 @@ pk_status pk_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* const A_chunk
     a.lda = lda;
     a.B = B; a.ldb = ldb;
     a.C = C; a.ldc = ldc;
-    const pk::TileCfgId cfg = pick_store_cfg(M, N);
+    const pk::TileCfgId cfg = with_staging(pick_store_cfg(M, N), K);
     const pk::TileShape t = pk::tile_shape(cfg);
     const int tiles_m = (int)ceil_div(M, t.bm);
     a.rot_tile_rows = (int)(((int64_t)first_chunk * chunk_rows) / t.bm) % tiles_m;
@@ -199,7 +206,7 @@ pk_status pk_gemm_reduce(int64_t M, int64_t N, int64_t K, const uint16_t* A, int
         const pk::Epi epi = mode == PK_REDUCE_ATOMIC ? pk::EPI_ATOMIC_F32
                             : fused_cast             ? pk::EPI_OWNER_CAST
                                                      : pk::EPI_OWNER_F32;
-        pk_status st = hip_status(pk::launch_gemm(a, pick_reduce_cfg(M, N), epi, s),
+        pk_status st = hip_status(pk::launch_gemm(a, with_staging(pick_reduce_cfg(M, N), K), epi, s),
                                   "pk_gemm_reduce launch");
         if (st != PK_OK) return st;
         if (fused_cast) return ok();

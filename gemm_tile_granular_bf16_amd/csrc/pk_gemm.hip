@@ -15,9 +15,11 @@
 //    4 consecutive columns, which the store and read-modify-write epilogues move as 16-byte
 //    vectors.  The atomic epilogue keeps the natural orientation (32 lanes on 32 consecutive
 //    columns of one row), which coalesces per-element atomics.
-//  * Operand staging without registers: both operands go HBM -> LDS with global_load_lds_dwordx4
-//    (each lane moves 16 bytes into its slot of a 1 KB wave-contiguous LDS block), so a whole
-//    stage is in flight while the previous one feeds the MFMAs.  A (M x K, k-contiguous) is
+//  * Operand staging: both operands go HBM -> LDS with global_load_lds_dwordx4 (each lane moves
+//    16 bytes into its slot of a 1 KB wave-contiguous LDS block), so a whole stage is in flight
+//    while the previous one feeds the MFMAs.  The 256x256 tile of a dense product with whole
+//    k-steps instead moves steps 2.. through registers (global_load_dwordx4, then ds_write_b128
+//    into the same LDS positions at the start of the next step), which measured faster.  A (M x K, k-contiguous) is
 //    stored as rows of BK bf16; B (K x N, n-contiguous) is stored as it is in memory, rows of BN
 //    bf16, and read with ds_read_b64_tr_b16, whose 16-lane transpose hands each lane the 4
 //    consecutive k of one column that the MFMA B operand wants (two reads give the 8 k of one
@@ -43,9 +45,13 @@
 namespace pk {
 
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int ST_, int WG_PER_CU_ = 1>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int ST_, int WG_PER_CU_ = 1,
+          bool REGS_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, ST = ST_, WG_PER_CU = WG_PER_CU_;
+    // REGS: k-steps 2.. go HBM -> registers -> LDS (one register stage, two LDS slots); dense
+    // products with K a multiple of BK only
+    static constexpr bool REGS = REGS_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -63,16 +69,19 @@ struct Cfg {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 MFMA blocks");
     static_assert(LDS_BYTES * WG_PER_CU <= 160 * 1024, "LDS is 160 KB per CU");
     static_assert(ST >= 2 && ST <= 5, "pipeline depth");
+    static_assert(!REGS || (ST == 2 && KK >= 2), "register staging uses two LDS slots");
 };
 
 using Cfg256x256 = Cfg<256, 256, 64, 2, 4, 2>;     // 8 waves of 128x64, 128 KB LDS
 using Cfg256x128 = Cfg<256, 128, 64, 2, 2, 3>;     // 4 waves of 128x64, 144 KB LDS
 using Cfg128x128 = Cfg<128, 128, 64, 2, 2, 2>;     // 4 waves of 64x64, 64 KB LDS
+using Cfg256x256R = Cfg<256, 256, 64, 2, 4, 2, 1, true>;  // the same, register-staged
 
 TileShape tile_shape(TileCfgId cfg) {
     switch (cfg) {
         case CFG_256x256: return {256, 256};
         case CFG_256x128: return {256, 128};
+        case CFG_256x256R: return {256, 256};
         default: return {128, 128};
     }
 }
@@ -189,13 +198,16 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
     // DMA block b = j*NW + w covers LDS bytes [b*1 KB, (b+1)*1 KB) of the stage's A (or B) part;
     // lane i owns 16-byte position q = b*64 + i.
     const uint16_t* a_src[C::AI];
-    int a_kc[C::AI];  // first k of this lane's chunk, relative to the step
+    auto a_kc = [&](int j) {
+        const int q = (j * C::NW + w) * 64 + lane;
+        return ((q % C::CPRA) ^ swz_a<C::CPRA>(q / C::CPRA)) * 8;
+    };
 #pragma unroll
     for (int j = 0; j < C::AI; ++j) {
         const int q = (j * C::NW + w) * 64 + lane;
         const int rl = q / C::CPRA;
         const int c = (q % C::CPRA) ^ swz_a<C::CPRA>(rl);
-        a_kc[j] = c * 8;
+
         int64_t r = row0 + rl;
         if (r >= row_end) r = row0;  // masked row: read a valid one, never stored
         const uint16_t* src;
@@ -208,16 +220,15 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
             const int ch = (int)(r / p.chunk_rows);
             src = pick(p.a_ptr, ch) + (r - (int64_t)ch * p.chunk_rows) * p.lda;
         }
-        a_src[j] = src + a_kc[j];
+        a_src[j] = src + c * 8;
     }
     const uint16_t* b_src[C::BI];
-    int b_kr[C::BI];  // k row of this lane's chunk, relative to the step
+    auto b_kr = [&](int j) { return ((j * C::NW + w) * 64 + lane) / C::CPRB; };
 #pragma unroll
     for (int j = 0; j < C::BI; ++j) {
         const int q = (j * C::NW + w) * 64 + lane;
         const int kr = q / C::CPRB;
         const int c = (q % C::CPRB) ^ swz_b<C::CPRB>(kr);
-        b_kr[j] = kr;
         int64_t col = col0 + c * 8;
         if (col >= N) col = 0;  // masked columns: read valid memory, never stored
         b_src[j] = Bm + (int64_t)kr * p.ldb + col;
@@ -241,22 +252,23 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
 #pragma unroll
         for (int j = 0; j < C::AI; ++j) {
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (k0 + a_kc[j] < K) v = *(const u32x4*)(a_src[j] + k0);
+            if (k0 + a_kc(j) < K) v = *(const u32x4*)(a_src[j] + k0);
             *(u32x4*)(sa + (j * C::NW + w) * 1024 + lane * 16) = v;
         }
 #pragma unroll
         for (int j = 0; j < C::BI; ++j) {
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (k0 + b_kr[j] < K) v = *(const u32x4*)(b_src[j] + k0 * p.ldb);
+            if (k0 + b_kr(j) < K) v = *(const u32x4*)(b_src[j] + k0 * p.ldb);
             *(u32x4*)(sb + (j * C::NW + w) * 1024 + lane * 16) = v;
         }
     };
 
     // ---- per-lane LDS read offsets ------------------------------------------------------------
     // A operand of block fm, slice kk: row wy*WTM + fm*32 + lane%32, k chunk 2*kk + lane/32.
-    int a_off[C::FM][C::KK];
+    constexpr int FMO = C::FM < 2 ? C::FM : 2;
+    int a_off[FMO][C::KK];
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
+    for (int fm = 0; fm < FMO; ++fm) {
         const int r = wy * C::WTM + fm * 32 + (lane & 31);
 #pragma unroll
         for (int kk = 0; kk < C::KK; ++kk)
@@ -287,7 +299,8 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
         const char* sa = lds + slot * C::STAGE;
         const char* sb = sa + C::A_BYTES;
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) af[fm] = *(const bf16x8*)(sa + a_off[fm][kk]);
+        for (int fm = 0; fm < C::FM; ++fm)
+            af[fm] = *(const bf16x8*)(sa + a_off[fm & 1][kk] + (fm >> 1) * 64 * (C::BK * 2));
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
             const char* q = sb + b_off[fn] + kk * 16 * (C::BN * 2);
@@ -329,7 +342,91 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
         if constexpr (C::ST >= 3) if (later >= 1) { wait_vmcnt<C::LPS>(); return; }
         wait_vmcnt<0>();
     };
-    if (nkl > 0) {
+    if constexpr (C::REGS) {
+        // Register-staged pipeline (whole k-steps only: the host picks this configuration when
+        // K % BK == 0).  Step j computes from LDS slot j % 2.  At its start it writes the
+        // registers, which hold step j+1, into the other slot (read in step j-1, before the
+        // barrier that ended it) and refills each register with step j+2 right after its write,
+        // so a step's loads have a whole step to land; one barrier per step.
+        constexpr int NSTG = C::AI + C::BI;
+        u32x4 stg[NSTG];
+        auto load_one = [&](int i, int64_t kt) {
+            const int64_t k0 = kt * C::BK;
+            const uint16_t* src = i < C::AI ? a_src[i] + k0 : b_src[i - C::AI] + k0 * p.ldb;
+            stg[i] = *(const u32x4*)src;
+        };
+        auto write_one = [&](int i, int slot) {
+            char* const sa = lds + slot * C::STAGE;
+            char* dst = i < C::AI ? sa + (i * C::NW + w) * 1024 + lane * 16
+                                  : sa + C::A_BYTES + ((i - C::AI) * C::NW + w) * 1024 + lane * 16;
+            *(u32x4*)dst = stg[i];
+        };
+        if (nkl > 0) {
+            // prologue: steps 0 and 1 go straight to LDS slots 0 and 1; the register pipeline
+            // starts with step 2, loaded during step 0
+            issue(kt_begin, 0);
+            if (nkl > 1) { issue(kt_begin + 1, 1); wait_vmcnt<C::LPS>(); }
+            else wait_vmcnt<0>();
+            wait_lgkmcnt0();
+            __builtin_amdgcn_s_barrier();
+            bf16x8 fa[2][C::FM], fb[2][C::FN];
+            read_frags(0, 0, fa[0], fb[0]);
+            constexpr int NR = C::FM + 2 * C::FN;
+            constexpr int NM = C::FM * C::FN;
+            // NEXT: a step j+1 follows; WRITE: the registers hold step j+1 (written to the other
+            // slot at the start); LOAD: refill them with step j+2; DMAW: step j+1 came by DMA
+            // (step 0 only), so wait for it explicitly, the register loads being younger.
+            auto step = [&](int64_t j, auto next_c, auto write_c, auto load_c, auto dmaw_c) {
+                constexpr bool NEXT = decltype(next_c)::value, WRITE = decltype(write_c)::value;
+                constexpr bool LOAD = decltype(load_c)::value, DMAW = decltype(dmaw_c)::value;
+                const int slot = (int)(j & 1), nslot = slot ^ 1;
+                if constexpr (WRITE || LOAD) {
+#pragma unroll
+                    for (int i = 0; i < NSTG; ++i) {
+                        if constexpr (WRITE) write_one(i, nslot);
+                        if constexpr (LOAD) load_one(i, kt_begin + j + 2);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int kk = 0; kk < C::KK; ++kk) {
+                    const int nb = (kk + 1) & 1;
+                    if (kk + 1 < C::KK) {
+                        read_frags(slot, kk + 1, fa[nb], fb[nb]);
+                        mfmas(fa[kk & 1], fb[kk & 1]);
+#pragma unroll
+                        for (int q = 0; q < NM; ++q) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        }
+                    } else if constexpr (NEXT) {
+                        wait_lgkmcnt0();
+                        if constexpr (DMAW) {
+                            if constexpr (LOAD) wait_vmcnt<NSTG>();
+                            else wait_vmcnt<0>();
+                        }
+                        __builtin_amdgcn_s_barrier();
+                        read_frags(nslot, 0, fa[nb], fb[nb]);
+                        mfmas(fa[kk & 1], fb[kk & 1]);
+                    } else {
+                        mfmas(fa[kk & 1], fb[kk & 1]);
+                    }
+                }
+            };
+            using TT = std::true_type;
+            using FF = std::false_type;
+            if (nkl == 1) {
+                step(0, FF{}, FF{}, FF{}, FF{});
+            } else {
+                if (nkl > 2) step(0, TT{}, FF{}, TT{}, TT{});
+                else step(0, TT{}, FF{}, FF{}, TT{});
+                int64_t j = 1;
+                for (; j + 2 < nkl; ++j) step(j, TT{}, TT{}, TT{}, FF{});
+                if (j + 1 < nkl) { step(j, TT{}, TT{}, FF{}, FF{}); ++j; }
+                step(j, FF{}, FF{}, FF{}, FF{});
+            }
+        }
+    } else if (nkl > 0) {
         // prologue: steps 0 .. ST-2 in flight, wait for step 0, then refill with step ST-1
 #pragma unroll
         for (int st = 0; st < C::ST - 1; ++st)
@@ -691,6 +788,9 @@ static hipError_t launch_cfg(const GemmArgs& a, TileCfgId cfg, Epi epi, int64_t 
         case CFG_256x256: return launch_epi<Cfg256x256, GROUPED>(a, epi, tiles, stream);
         case CFG_256x128: return launch_epi<Cfg256x128, GROUPED>(a, epi, tiles, stream);
         case CFG_128x128: return launch_epi<Cfg128x128, GROUPED>(a, epi, tiles, stream);
+        case CFG_256x256R:
+            if constexpr (!GROUPED) return launch_epi<Cfg256x256R, false>(a, epi, tiles, stream);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }

@@ -39,6 +39,9 @@ SHAPES = [  # (M, N, K, chunks, first_chunk): tails in every dimension, every ti
     (700, 520, 96, 5, 4),
     (4100, 2056, 72, 4, 1),    # 256x128 tiles
     (8200, 4104, 72, 2, 1),    # 256x256 tiles, ragged in M and N, K tail
+    (8200, 4104, 64, 2, 1),    # 256x256 tiles staged through registers: one k-step
+    (8200, 4104, 128, 1, 0),   # two k-steps (both by direct loads)
+    (8200, 4104, 192, 3, 2),   # three k-steps (the third through registers)
 ]
 
 

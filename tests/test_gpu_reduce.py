@@ -146,16 +146,17 @@ def test_ragged_shards_with_bf16_output(pk, oracle_mod, mode):
     assert np.all(out[:, N:] == 0x40e0)  # bf16 bits of 7.0
 
 
+@pytest.mark.parametrize("K", [72, 320], ids=["K72", "K320"])
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
-def test_large_ragged_with_straddling_shards(pk, oracle_mod, mode):
-    """More 256x256 tiles (17 x 33) than the device runs workgroups at once, ragged in every
-    dimension, shards of 544 rows (128-row bands of the owner epilogue straddle shard
-    boundaries, which takes its per-row shard path), padded leading dimensions and the bf16
-    output."""
-    M, N, K = 4200, 8200, 72
+def test_large_ragged_with_straddling_shards(pk, oracle_mod, mode, K):
+    """More 256x256 tiles (17 x 33) than the device runs workgroups at once, ragged in M and N,
+    shards of 544 rows (128-row bands of the owner epilogue straddle shard boundaries, which takes
+    its per-row shard path), padded leading dimensions and the bf16 output.  K = 72 ends in a
+    ragged k-step (direct-to-LDS loop); K = 320 is five whole k-steps (register-staged loop)."""
+    M, N = 4200, 8200
     log("pk_gemm_reduce large ragged M=%d N=%d K=%d mode=%d" % (M, N, K, mode))
-    A = pk_inputs.normal_bf16((M, K), 1.0, 131)
-    B = pk_inputs.normal_bf16((K, N), 1.0, 132)
+    A = pk_inputs.normal_bf16((M, K), 1.0, 131 + K)
+    B = pk_inputs.normal_bf16((K, N), 1.0, 132 + K)
     D0 = np.random.Generator(np.random.PCG64(133)).standard_normal((M, N)).astype(np.float32)
     base = torch.zeros((M, N + 24), device="cuda")
     base[:, :N] = torch.from_numpy(D0).cuda()
