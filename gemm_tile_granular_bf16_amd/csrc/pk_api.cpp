@@ -78,11 +78,15 @@ pk::TileCfgId pick_store_cfg(int64_t M, int64_t N) {
 // Tile shape for the reduction epilogues: the same rule as the stores.
 pk::TileCfgId pick_reduce_cfg(int64_t M, int64_t N) { return pick_store_cfg(M, N); }
 
-// The 256x256 tile stages k-steps through registers when every k-step is whole (measured faster
-// than direct-to-LDS loads on the 8192^2 x 1024 and 16384^2 x 2048 shares); a ragged last k-step
-// keeps the direct-to-LDS loop, which zero-fills it.
+// The 256-row tiles stage k-steps 2.. through registers when every k-step is whole (measured
+// faster than direct-to-LDS loads on every full-size workload: the RS, AR and AG shares and the
+// grouped expert products); a ragged last k-step keeps the direct-to-LDS loop, which zero-fills
+// it.
 pk::TileCfgId with_staging(pk::TileCfgId cfg, int64_t K) {
-    return cfg == pk::CFG_256x256 && K % 64 == 0 ? pk::CFG_256x256R : cfg;
+    if (K % 64 != 0) return cfg;
+    if (cfg == pk::CFG_256x256) return pk::CFG_256x256R;
+    if (cfg == pk::CFG_256x128) return pk::CFG_256x128R;
+    return cfg;
 }
 
 }  // namespace
@@ -256,7 +260,7 @@ pk_status pk_grouped_gemm(int64_t T, int top_k, const int32_t* topk_ids, int num
     int32_t* tile_offsets = slice_counts + (size_t)plan.num_slices * num_local;
     int32_t* counters = (int32_t*)((char*)workspace + gw.counters_off);
     float* partials = (float*)((char*)workspace + gw.partials_off);
-    const pk::TileCfgId cfg = kGroupedCfg;
+    const pk::TileCfgId cfg = with_staging(kGroupedCfg, K);
     const pk::TileShape t = pk::tile_shape(cfg);
     hipError_t e = pk::launch_dispatch(plan, topk_ids, num_experts, expert_begin, num_local, t.bm,
                                        offsets, perm, tile_offsets, slice_counts, counters,
@@ -323,7 +327,7 @@ pk_status pk_grouped_combine(int64_t T, int top_k, int num_local, const int32_t*
     if (K == 0) return ok();  // nothing to add
 
     hipStream_t s = (hipStream_t)stream;
-    const pk::TileCfgId cfg = kGroupedCfg;
+    const pk::TileCfgId cfg = with_staging(kGroupedCfg, K);
     const pk::TileShape t = pk::tile_shape(cfg);
     int32_t* tile_offsets = (int32_t*)workspace;
     hipError_t e = pk::launch_tile_prefix(offsets, num_local, t.bm, tile_offsets, s);

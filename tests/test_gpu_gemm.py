@@ -38,6 +38,8 @@ SHAPES = [  # (M, N, K, chunks, first_chunk): tails in every dimension, every ti
     (256, 256, 64, 1, 0),
     (700, 520, 96, 5, 4),
     (4100, 2056, 72, 4, 1),    # 256x128 tiles
+    (4100, 2056, 128, 4, 1),   # 256x128 tiles, two whole k-steps (register-staged loop)
+    (4100, 2056, 320, 2, 0),   # 256x128 tiles, five whole k-steps
     (8200, 4104, 72, 2, 1),    # 256x256 tiles, ragged in M and N, K tail
     (8200, 4104, 64, 2, 1),    # 256x256 tiles staged through registers: one k-step
     (8200, 4104, 128, 1, 0),   # two k-steps (both by direct loads)
