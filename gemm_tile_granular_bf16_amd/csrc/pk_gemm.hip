@@ -200,6 +200,7 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
     // DMA block b = j*NW + w covers LDS bytes [b*1 KB, (b+1)*1 KB) of the stage's A (or B) part;
     // lane i owns 16-byte position q = b*64 + i.
     const uint16_t* a_src[C::AI];
+    // first k of this lane's A chunk j, relative to the step (needed only for a ragged step)
     auto a_kc = [&](int j) {
         const int q = (j * C::NW + w) * 64 + lane;
         return ((q % C::CPRA) ^ swz_a<C::CPRA>(q / C::CPRA)) * 8;
@@ -225,6 +226,7 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
         a_src[j] = src + c * 8;
     }
     const uint16_t* b_src[C::BI];
+    // k row of this lane's B chunk j, relative to the step (needed only for a ragged step)
     auto b_kr = [&](int j) { return ((j * C::NW + w) * 64 + lane) / C::CPRB; };
 #pragma unroll
     for (int j = 0; j < C::BI; ++j) {
@@ -267,6 +269,9 @@ __global__ __launch_bounds__(C::NT, C::WG_PER_CU) void gemm_tile_kernel(GemmArgs
 
     // ---- per-lane LDS read offsets ------------------------------------------------------------
     // A operand of block fm, slice kk: row wy*WTM + fm*32 + lane%32, k chunk 2*kk + lane/32.
+    // Blocks fm and fm + 2 are 64 rows apart, and the swizzle sees a row only through row % 64
+    // (row % 8 and (row / 8) % 8, or fewer bits for 64-byte rows), where they agree: two offset
+    // sets serve every block, the rest being an immediate offset of the LDS read.
     constexpr int FMO = C::FM < 2 ? C::FM : 2;
     int a_off[FMO][C::KK];
 #pragma unroll
