@@ -74,9 +74,12 @@ def test_dispatch_special_cases(pk, oracle_mod):
         _check_dispatch(o, ids, E, begin, nl, off, perm)
 
 
+@pytest.mark.parametrize("K", [136, 320], ids=["K136", "K320"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-def test_grouped_parity_small(pk, oracle_mod, dtype):
-    T, top_k, E, begin, nl, K, N = 300, 4, 16, 3, 6, 136, 264
+def test_grouped_parity_small(pk, oracle_mod, dtype, K):
+    """K = 136 ends in a ragged k-step (direct-to-LDS loop); K = 320 is five whole k-steps
+    (register-staged loop); the split tail cuts every tile into single-step pieces."""
+    T, top_k, E, begin, nl, N = 300, 4, 16, 3, 6, 264
     ids = pk_inputs.zipf_topk(T, E, top_k, 0.9, 21)
     X = pk_inputs.normal_bf16((T, K), 1.0, 22)
     W = pk_inputs.normal_bf16((nl, K, N), 0.5, 23)
